@@ -1,0 +1,194 @@
+/*
+ * bi.h -- C ABI of the batch-invariant forward kernels for MI355X (gfx950).
+ *
+ * Three operations of a Llama-style decoder layer's forward pass -- a bf16
+ * GEMM, RMSNorm and paged decode attention -- each written so that every
+ * output row's floating-point reduction order is a function of that row's own
+ * data only: never of the batch size M, of the other requests in the batch,
+ * of where their KV pages sit, of the longest context, or of how many compute
+ * units are free.  Each has a "_fast" twin with the same signature that picks
+ * its schedule from the batch shape and the CU count (deterministic from run
+ * to run, but not batch-invariant); the twins exist to measure the cost of
+ * invariance.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [Article] "LLM inference determinism engineering in depth: from float
+ *             non-associativity and batch invariance to reproducible kernels"
+ *             (ybb.press, ai-applications/14528).
+ *   [LLM-42]  "LLM-42: Enabling Determinism in LLM Inference with Verified
+ *             Speculation (SOSP 2026)", ai-infra-wiki digest.
+ *   [Vosti]   arxivdaily 2609.38981, abstract of the Vosti engine.
+ *
+ * Conventions for every call:
+ *   - Pointers named x, W, y, g, q, kv_pages, block_table, ctx_lens, out and
+ *     ws are DEVICE pointers, owned by the caller, 16-byte aligned.  The
+ *     library allocates and frees nothing inside a call.
+ *   - bf16 values are passed as raw bits (bi_bf16).  Matrices are row-major
+ *     and contiguous.
+ *   - stream is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work and return; a device-side fault surfaces at the caller's next
+ *     synchronisation.
+ *   - Errors are reported by the return code only; nothing is printed and
+ *     nothing aborts.  On an error nothing is enqueued.
+ *   - Workspace: operations that need one take (ws, ws_bytes), sized by the
+ *     matching *_workspace_bytes query.  The first BI_WS_COUNTER_BYTES of a
+ *     workspace hold integer arrival counters: they must be zero before the
+ *     first call that uses the workspace (e.g. one hipMemset after
+ *     allocating it), and every completed call leaves them zero again.  One
+ *     workspace may be reused by any sequence of calls on one stream;
+ *     concurrent calls must use distinct workspaces.
+ *   - No global mutable state: concurrent calls on different streams with
+ *     distinct workspaces are safe.
+ *   - Determinism contract (bi_* entry points, not the _fast twins): the
+ *     output bits of a row/request depend only on that row's/request's
+ *     inputs, the weights, gain or logical KV contents, the library version
+ *     and the gfx target.  Plan choice reads only (N, K), H, or
+ *     (D, page size, Hq, Hkv).  ([Article] section 4: the reduction order must
+ *     depend on the data only; [Vosti]: kernel choice independent of engine
+ *     state, cached KV bound to its logical token position.)
+ */
+#ifndef BI_H
+#define BI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t bi_bf16;
+
+enum {
+    BI_OK = 0,
+    BI_ERR_NULL = -1,        /* a required pointer is NULL                   */
+    BI_ERR_SHAPE = -2,       /* a size is <= 0 or a size product overflows   */
+    BI_ERR_UNSUPPORTED = -3, /* shape outside what the kernels handle, or a
+                                pointer not 16-byte aligned                   */
+    BI_ERR_WORKSPACE = -4,   /* ws is NULL or ws_bytes smaller than needed   */
+    BI_ERR_HIP = -5          /* the HIP launch itself failed                 */
+};
+
+/* Bytes at the start of every workspace that hold arrival counters. */
+#define BI_WS_COUNTER_BYTES 65536
+
+/* Library version, gfx target and every schedule constant, as one static
+ * NUL-terminated string.  [Article] section 6: record the exact kernel
+ * library and compile flags next to every result. */
+const char *bi_version(void);
+
+/* Static text for a status code. */
+const char *bi_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * GEMM:  y[M,N] = bf16_rne( x[M,K] . W[K,N] ),  bf16 in, fp32 accumulate.
+ *
+ * [Article] section 1 (the batch-1 vs batch-8 linear layer), section 2.2
+ * (shape-dependent tiling and split-k with float atomics break invariance),
+ * section 4 (fixed M tile with padding; K split only into fixed segments whose
+ * partial sums go to a fixed workspace and are added in index order; no float
+ * atomics), section 5 (no reduced-precision intermediate reduction).
+ *
+ * Schedule of bi_gemm (fixed by K only): K-blocks of 32 (one
+ * v_mfma_f32_16x16x32_bf16), segments of 512 accumulated from +0, segments
+ * added left to right 0..S-1 in fp32, S = ceil(K/512), one RNE narrowing.
+ *
+ * x: [M,K] bf16 row-major.  W: [K,N] bf16 row-major (y = x times W, as the
+ * article's section-1 demo multiplies).  y: [M,N] bf16 row-major, written
+ * only for rows < M.  Requirements: M, N, K >= 1; K % 32 == 0; N % 64 == 0;
+ * M*K, K*N, M*N < 2^31; else BI_ERR_SHAPE / BI_ERR_UNSUPPORTED.
+ * ws/ws_bytes: workspace of at least bi_gemm_workspace_bytes(M,N,K) bytes
+ * (fp32 segment partials plus the counter region).
+ * ---------------------------------------------------------------------- */
+size_t bi_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int bi_gemm(const bi_bf16 *x, const bi_bf16 *W, bi_bf16 *y,
+            int64_t M, int64_t N, int64_t K,
+            void *ws, size_t ws_bytes, void *stream);
+
+/* Same operation with tiles and K split chosen from (M, N, K) and the CU
+ * count.  Deterministic run to run (ordered workspace, no float atomics) but
+ * NOT batch-invariant.  Same arguments and requirements. */
+size_t bi_gemm_fast_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int bi_gemm_fast(const bi_bf16 *x, const bi_bf16 *W, bi_bf16 *y,
+                 int64_t M, int64_t N, int64_t K,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * RMSNorm:  y[m,h] = bf16_rne( (x[m,h] * r_m) * g[h] ),
+ *           r_m = 1 / sqrt( (sum_h x[m,h]^2) / H + eps ),  fp32 throughout.
+ *
+ * [LLM-42] problem statement and [Article] section 2.2: normalization is one
+ * of the reductions whose schedule a dynamic batch changes.  bi_rmsnorm
+ * reduces each row in one workgroup of 256 lanes with a fixed tree (per-lane
+ * strided sums, a 64-lane xor butterfly, four wave sums added in order);
+ * sqrt and the division are correctly rounded.
+ *
+ * x: [M,H] bf16.  g: [H] bf16.  y: [M,H] bf16 (may not alias x).
+ * Requirements: M, H >= 1; H % 8 == 0; M*H < 2^31.  No workspace.
+ * ---------------------------------------------------------------------- */
+int bi_rmsnorm(const bi_bf16 *x, const bi_bf16 *g, bi_bf16 *y,
+               int64_t M, int64_t H, float eps, void *stream);
+
+/* Rows per workgroup and lanes per row chosen from M; not batch-invariant. */
+int bi_rmsnorm_fast(const bi_bf16 *x, const bi_bf16 *g, bi_bf16 *y,
+                    int64_t M, int64_t H, float eps, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Paged decode attention (one query token per request, GQA):
+ *   out[b,h,:] = softmax_t( scale * q[b,h,:] . k_t ) . v_t,  t < ctx_lens[b],
+ *   kv head of q head h = h / (num_q_heads / num_kv_heads).
+ *
+ * [Vosti] abstract: outputs must not change with the batch or with the paged
+ * KV-cache layout.  [Article] section 4: split work only at boundaries fixed
+ * by the data and combine partials in a fixed order.  bi_paged_decode_attn
+ * cuts every request's context into chunks of 256 tokens (tiles of 64 inside
+ * a chunk, online softmax), whatever the batch, and combines the chunk
+ * partials in chunk order.
+ *
+ * q:           [batch, num_q_heads, head_dim] bf16.
+ * kv_pages:    [num_pages, 2 (K then V), num_kv_heads, page_size, head_dim]
+ *              bf16; one (page, K|V, kv head) block is contiguous.
+ * block_table: [batch, max_blocks_per_seq] int32; token t of request b sits
+ *              in page block_table[b][t / page_size], slot t % page_size.
+ *              Entries past a request's last page are never read.
+ * ctx_lens:    [batch] int32, read on the device; a request with
+ *              ctx_lens[b] <= 0 gets zeros.  Every ctx_lens[b] must be
+ *              <= max_ctx_len and every referenced page < num_pages (device
+ *              data is not range-checked).
+ * out:         [batch, num_q_heads, head_dim] bf16.
+ * Supported: head_dim == 128, page_size == 16, num_q_heads % num_kv_heads
+ * == 0 with num_q_heads / num_kv_heads <= 8, batch >= 1, 1 <= max_ctx_len
+ * <= max_blocks_per_seq * page_size.  max_ctx_len only sizes the grid and
+ * the workspace; it never changes the bits.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t max_blocks_per_seq;
+    int64_t num_pages;
+    int32_t max_ctx_len;
+    float scale; /* usually 1/sqrt(head_dim) */
+} bi_attn_desc;
+
+size_t bi_attn_workspace_bytes(const bi_attn_desc *d);
+int bi_paged_decode_attn(const bi_bf16 *q, const bi_bf16 *kv_pages,
+                         const int32_t *block_table, const int32_t *ctx_lens,
+                         bi_bf16 *out, const bi_attn_desc *d,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* Number of KV splits chosen from batch * num_kv_heads against the CU count
+ * (split boundaries then depend on the batch): not batch-invariant. */
+size_t bi_attn_fast_workspace_bytes(const bi_attn_desc *d);
+int bi_paged_decode_attn_fast(const bi_bf16 *q, const bi_bf16 *kv_pages,
+                              const int32_t *block_table,
+                              const int32_t *ctx_lens, bi_bf16 *out,
+                              const bi_attn_desc *d, void *ws, size_t ws_bytes,
+                              void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BI_H */

@@ -1,0 +1,23 @@
+"""Batch-invariant forward kernels for MI355X (gfx950): Python binding.
+
+Thin argument marshalling over the C-ABI library ``libbi.so`` (declared in
+``include/bi.h``).  Every step of the computation runs in the library's HIP
+kernels; torch supplies device memory and the current stream only.  There is
+no CPU or library fallback: if the HIP library is missing, every call raises.
+"""
+from ._lib import (  # noqa: F401
+    BiError,
+    load,
+    version,
+    gemm,
+    gemm_fast,
+    gemm_workspace_bytes,
+    gemm_fast_workspace_bytes,
+    rmsnorm,
+    rmsnorm_fast,
+    paged_decode_attn,
+    paged_decode_attn_fast,
+    attn_workspace_bytes,
+    attn_fast_workspace_bytes,
+    Workspace,
+)

@@ -1,0 +1,263 @@
+"""ctypes binding of libbi.so (argument marshalling only).
+
+Tensors are torch device tensors; the library receives their raw device
+pointers and torch's current HIP stream.  Nothing here computes: a missing
+library raises instead of falling back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbi.so")
+WS_COUNTER_BYTES = 65536
+
+_STATUS = {0: "BI_OK", -1: "BI_ERR_NULL", -2: "BI_ERR_SHAPE", -3: "BI_ERR_UNSUPPORTED",
+           -4: "BI_ERR_WORKSPACE", -5: "BI_ERR_HIP"}
+
+
+class BiError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)} ({status})")
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64), ("max_ctx_len", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+EXPORTS = ("bi_version", "bi_status_string", "bi_gemm_workspace_bytes", "bi_gemm",
+           "bi_gemm_fast_workspace_bytes", "bi_gemm_fast", "bi_rmsnorm", "bi_rmsnorm_fast",
+           "bi_attn_workspace_bytes", "bi_paged_decode_attn", "bi_attn_fast_workspace_bytes",
+           "bi_paged_decode_attn_fast")
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libbi.so once; raise if it was never built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                f"HIP library {p} is missing: build it first (python -c 'import __graft_entry__ as "
+                f"g; g.build()'); there is no fallback path")
+        lib = ctypes.CDLL(p)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        lib.bi_version.restype = ctypes.c_char_p
+        lib.bi_version.argtypes = []
+        lib.bi_status_string.restype = ctypes.c_char_p
+        lib.bi_status_string.argtypes = [ctypes.c_int]
+        for f in ("bi_gemm_workspace_bytes", "bi_gemm_fast_workspace_bytes"):
+            getattr(lib, f).restype = sz
+            getattr(lib, f).argtypes = [i64, i64, i64]
+        for f in ("bi_gemm", "bi_gemm_fast"):
+            getattr(lib, f).restype = ctypes.c_int
+            getattr(lib, f).argtypes = [vp, vp, vp, i64, i64, i64, vp, sz, vp]
+        for f in ("bi_rmsnorm", "bi_rmsnorm_fast"):
+            getattr(lib, f).restype = ctypes.c_int
+            getattr(lib, f).argtypes = [vp, vp, vp, i64, i64, ctypes.c_float, vp]
+        for f in ("bi_attn_workspace_bytes", "bi_attn_fast_workspace_bytes"):
+            getattr(lib, f).restype = sz
+            getattr(lib, f).argtypes = [ctypes.POINTER(AttnDesc)]
+        for f in ("bi_paged_decode_attn", "bi_paged_decode_attn_fast"):
+            getattr(lib, f).restype = ctypes.c_int
+            getattr(lib, f).argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(AttnDesc), vp, sz, vp]
+        _lib = lib
+        return lib
+
+
+def version() -> str:
+    return load().bi_version().decode()
+
+
+class Workspace:
+    """A zero-initialised device workspace that grows on demand.
+
+    The library needs the first 64 KiB (arrival counters) to be zero on entry
+    and leaves them zero; the rest is scratch.  One Workspace per stream.
+    """
+
+    def __init__(self, device=None):
+        self.device = torch.device(device or "cuda")
+        self.buf = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        nbytes = max(int(nbytes), WS_COUNTER_BYTES)
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_default_ws: dict = {}
+
+
+def _ws_for(device: torch.device, ws: Workspace | None) -> Workspace:
+    if ws is not None:
+        return ws
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    w = _default_ws.get(key)
+    if w is None:
+        w = _default_ws[key] = Workspace(device)
+    return w
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_bf16(t: torch.Tensor, name: str, ndim: int):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be a bfloat16 tensor")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-D tensor")
+
+
+def _raise(status: int, where: str):
+    if status != 0:
+        raise BiError(status, where)
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load().bi_gemm_workspace_bytes(M, N, K))
+
+
+def gemm_fast_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load().bi_gemm_fast_workspace_bytes(M, N, K))
+
+
+def _gemm(fn_name, wsq, x, w, out, ws):
+    lib = load()
+    _check_bf16(x, "x", 2)
+    _check_bf16(w, "W", 2)
+    M, K = x.shape
+    K2, N = w.shape
+    if K != K2:
+        raise ValueError(f"x is [M,{K}] but W is [{K2},N]")
+    if x.device != w.device:
+        raise ValueError("x and W on different devices")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _check_bf16(out, "out", 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    need = int(getattr(lib, wsq)(M, N, K))
+    buf = _ws_for(x.device, ws).get(need)
+    st = getattr(lib, fn_name)(x.data_ptr(), w.data_ptr(), out.data_ptr(), M, N, K,
+                               buf.data_ptr(), buf.numel(), _stream(x.device))
+    _raise(st, fn_name)
+    return out
+
+
+def gemm(x, w, out=None, ws: Workspace | None = None):
+    """y = x @ W (batch-invariant).  x [M,K], W [K,N] bf16 device tensors."""
+    return _gemm("bi_gemm", "bi_gemm_workspace_bytes", x, w, out, ws)
+
+
+def gemm_fast(x, w, out=None, ws: Workspace | None = None):
+    """y = x @ W with M-tuned tiles and split (not batch-invariant)."""
+    return _gemm("bi_gemm_fast", "bi_gemm_fast_workspace_bytes", x, w, out, ws)
+
+
+def _rmsnorm(fn_name, x, g, eps, out):
+    lib = load()
+    _check_bf16(x, "x", 2)
+    _check_bf16(g, "g", 1)
+    M, H = x.shape
+    if g.shape[0] != H:
+        raise ValueError("gain must have shape [H]")
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_bf16(out, "out", 2)
+        if tuple(out.shape) != (M, H):
+            raise ValueError("out has the wrong shape")
+    st = getattr(lib, fn_name)(x.data_ptr(), g.data_ptr(), out.data_ptr(), M, H,
+                               ctypes.c_float(eps), _stream(x.device))
+    _raise(st, fn_name)
+    return out
+
+
+def rmsnorm(x, g, eps: float = 1e-5, out=None):
+    return _rmsnorm("bi_rmsnorm", x, g, eps, out)
+
+
+def rmsnorm_fast(x, g, eps: float = 1e-5, out=None):
+    return _rmsnorm("bi_rmsnorm_fast", x, g, eps, out)
+
+
+def _attn_desc(q, kv, block_table, max_ctx_len, scale):
+    B, Hq, D = q.shape
+    P, two, Hkv, PS, D2 = kv.shape
+    if two != 2 or D2 != D:
+        raise ValueError("kv_pages must be [P, 2, Hkv, page_size, head_dim]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [batch, max_blocks]")
+    if scale is None:
+        scale = float(torch.tensor(1.0, dtype=torch.float32) /
+                      torch.sqrt(torch.tensor(float(D), dtype=torch.float32)))
+    return AttnDesc(B, Hq, Hkv, D, PS, block_table.shape[1], P, int(max_ctx_len), scale)
+
+
+def attn_workspace_bytes(desc: AttnDesc) -> int:
+    return int(load().bi_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def attn_fast_workspace_bytes(desc: AttnDesc) -> int:
+    return int(load().bi_attn_fast_workspace_bytes(ctypes.byref(desc)))
+
+
+def _attn(fn_name, wsq, q, kv, block_table, ctx_lens, max_ctx_len, scale, out, ws):
+    lib = load()
+    _check_bf16(q, "q", 3)
+    _check_bf16(kv, "kv_pages", 5)
+    for t, n in ((block_table, "block_table"), (ctx_lens, "ctx_lens")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous int32 device tensor")
+    if ctx_lens.dim() != 1 or ctx_lens.shape[0] != q.shape[0]:
+        raise ValueError("ctx_lens must be [batch]")
+    if max_ctx_len is None:
+        max_ctx_len = int(ctx_lens.max().item())  # host sync; pass it to avoid one
+    desc = _attn_desc(q, kv, block_table, max(int(max_ctx_len), 1), scale)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bf16(out, "out", 3)
+        if out.shape != q.shape:
+            raise ValueError("out has the wrong shape")
+    need = int(getattr(lib, wsq)(ctypes.byref(desc)))
+    buf = _ws_for(q.device, ws).get(need)
+    st = getattr(lib, fn_name)(q.data_ptr(), kv.data_ptr(), block_table.data_ptr(),
+                               ctx_lens.data_ptr(), out.data_ptr(), ctypes.byref(desc),
+                               buf.data_ptr(), buf.numel(), _stream(q.device))
+    _raise(st, fn_name)
+    return out
+
+
+def paged_decode_attn(q, kv_pages, block_table, ctx_lens, max_ctx_len=None, scale=None,
+                      out=None, ws: Workspace | None = None):
+    """Batch-invariant paged decode attention (fixed 256-token chunks)."""
+    return _attn("bi_paged_decode_attn", "bi_attn_workspace_bytes", q, kv_pages, block_table,
+                 ctx_lens, max_ctx_len, scale, out, ws)
+
+
+def paged_decode_attn_fast(q, kv_pages, block_table, ctx_lens, max_ctx_len=None, scale=None,
+                           out=None, ws: Workspace | None = None):
+    """Paged decode attention with batch-dependent splits (not batch-invariant)."""
+    return _attn("bi_paged_decode_attn_fast", "bi_attn_fast_workspace_bytes", q, kv_pages,
+                 block_table, ctx_lens, max_ctx_len, scale, out, ws)
