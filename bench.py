@@ -1,0 +1,323 @@
+"""Benchmark of the batch-invariant forward path on one MI355X.
+
+One step = the four Llama-3-8B-shaped linears (qkv 4096->6144, o 4096->4096,
+gate_up 4096->28672, down 14336->4096) through bi_gemm at batch M (default
+2048), on seeded synthetic bf16 data resident in HBM.  ``value`` is the
+step's bi_gemm throughput in TFLOP/s.  The same run also reports, on the same
+kind of data:
+  * the decode regime (M = 16): GB/s against the HBM roofline;
+  * the invariance overhead t_bi / t_fast - 1 against the fast twins;
+  * bitwise mismatches between rows at M = 1 and the same rows in the batch;
+  * bi_rmsnorm (x[512,4096]) and bi_paged_decode_attn (64 requests, context
+    lengths uniform in [512, 32768]) with their HBM roofline fractions;
+  * the CPU oracle timed on host cores on a bounded sample (rows of the same
+    linears; row independence makes the sample exact).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--m 2048]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "bi_gemm TFLOP/s & GB/s vs roofline; invariance overhead %; mismatches=0"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix peak, published
+LINEARS = (("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 28672),
+           ("down", 14336, 4096))
+
+
+def gemm_flops(M, K, N):
+    return 2.0 * M * K * N
+
+
+def gemm_bytes(M, K, N):
+    return 2.0 * (M * K + K * N + M * N)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--m", type=int, default=2048)
+    p.add_argument("--decode-m", type=int, default=16)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="time only the main step (for profiler runs)")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="run only a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream the library launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def total_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs)
+
+    def mean_ms(self):
+        return self.total_ms() / max(1, len(self.pairs))
+
+
+def make_weights(torch, synth, copies, dev):
+    sets = []
+    for c in range(copies):
+        ws = {}
+        for i, (name, K, N) in enumerate(LINEARS):
+            ws[name] = synth.bf16_normal((K, N), seed=100 + 10 * c + i, std=0.02, device=dev)
+        sets.append(ws)
+    return sets
+
+
+def make_acts(torch, synth, M, dev, seed):
+    return {name: synth.bf16_normal((M, K), seed=seed + i, device=dev)
+            for i, (name, K, N) in enumerate(LINEARS)}
+
+
+def time_linears(torch, fn, acts, wsets, outs, steps, warmup, per_kernel=None):
+    """Run `steps` passes over the four linears, rotating weight copies."""
+    for s in range(warmup):
+        w = wsets[s % len(wsets)]
+        for name, K, N in LINEARS:
+            fn(acts[name], w[name], out=outs[name])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(steps):
+        w = wsets[s % len(wsets)]
+        for name, K, N in LINEARS:
+            if per_kernel is not None and name in per_kernel:
+                e = per_kernel[name].start()
+                fn(acts[name], w[name], out=outs[name])
+                per_kernel[name].stop(e)
+            else:
+                fn(acts[name], w[name], out=outs[name])
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
+def cpu_baseline(synth, oracle, M, budget_s=12.0):
+    """The oracle on whole rows of the four linears, all host cores."""
+    import numpy as np
+    cores = min(16, len(os.sched_getaffinity(0)))
+    rows_per_linear = max(1, cores)
+    jobs = []
+    for i, (name, K, N) in enumerate(LINEARS):
+        w = synth.to_bits(synth.bf16_normal((K, N), seed=100 + i, std=0.02))
+        x = synth.to_bits(synth.bf16_normal((rows_per_linear, K), seed=7 + i))
+        jobs.append((name, x, w, K, N))
+    flops = 0.0
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+        futs = []
+        for name, x, w, K, N in jobs:
+            for r in range(x.shape[0]):
+                futs.append(ex.submit(oracle.gemm, x[r:r + 1], w))
+                flops += gemm_flops(1, K, N)
+        for f in futs:
+            f.result()
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows_per_linear} rows of each of qkv/o/gate_up/down (one oracle call "
+                      f"per row, rows spread over {cores} threads); {dt:.1f} s; rows are "
+                      f"independent, so per-row cost is that of the M={M} batch"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import invariant_bi_gemm_02_amd as bi
+    from invariant_bi_gemm_02_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bi.load()
+
+    if args.calib_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "reads": n, "writes": n}))
+        return
+
+    M = args.m
+    wsets = make_weights(torch, synth, 2, dev)
+    acts = make_acts(torch, synth, M, dev, seed=1)
+    outs = {name: torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            for name, K, N in LINEARS}
+    per_kernel = {"gate_up": Timer(torch)}
+
+    ms_total = time_linears(torch, bi.gemm, acts, wsets, outs, args.steps, args.warmup,
+                            per_kernel)
+    ms_step = ms_total / args.steps
+    step_flops = sum(gemm_flops(M, K, N) for _, K, N in LINEARS)
+    value = step_flops / (ms_step * 1e-3) / 1e12
+
+    gu_ms = per_kernel["gate_up"].mean_ms()
+    K_gu, N_gu = 4096, 28672
+    bound_mfma = gemm_flops(M, K_gu, N_gu) / (MFMA_BF16_PEAK_TFS * 1e12) > \
+        gemm_bytes(M, K_gu, N_gu) / (HBM_PEAK_GBS * 1e9)
+    if bound_mfma:
+        ach = gemm_flops(M, K_gu, N_gu) / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": None,
+                "kernel": "gemm_tile_kernel<true> (gate_up 4096->28672)",
+                "avg_launch_us": gu_ms * 1e3}
+    else:
+        ach = gemm_bytes(M, K_gu, N_gu) / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "gemm_split_kernel (gate_up 4096->28672)",
+                "avg_launch_us": gu_ms * 1e3}
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"Llama-3-8B-shaped linears qkv/o/gate_up/down via bi_gemm, "
+                               f"x[{M},K] N(0,1), W[K,N] N(0,0.02), bf16, fp32 accumulate",
+                   "M": M, "linears": [list(l) for l in LINEARS]},
+        "roofline": roof,
+    }
+
+    if not args.no_extras:
+        extras = {}
+        # fast twin at the same M
+        ms_fast = time_linears(torch, bi.gemm_fast, acts, wsets, outs, args.steps,
+                               args.warmup) / args.steps
+        extras["overhead_pct_vs_fast"] = (ms_step / ms_fast - 1.0) * 100.0
+        extras["fast_tflops"] = step_flops / (ms_fast * 1e-3) / 1e12
+        # per-linear times at M and at decode M
+        per = {}
+        for Mx in sorted(set([M, args.decode_m, 1])):
+            ax = make_acts(torch, synth, Mx, dev, seed=1) if Mx != M else acts
+            ox = {name: torch.empty((Mx, N), dtype=torch.bfloat16, device=dev)
+                  for name, K, N in LINEARS}
+            row = {}
+            for fn_name, fn in (("bi", bi.gemm), ("fast", bi.gemm_fast)):
+                timers = {name: Timer(torch) for name, _, _ in LINEARS}
+                time_linears(torch, fn, ax, wsets, ox, max(4, args.steps // 2), 2, timers)
+                row[fn_name] = {name: timers[name].mean_ms() * 1e3 for name, _, _ in LINEARS}
+            lin = {}
+            for name, K, N in LINEARS:
+                tb, tf = row["bi"][name], row["fast"][name]
+                lin[name] = {"us": tb, "fast_us": tf, "overhead_pct": (tb / tf - 1) * 100,
+                             "tflops": gemm_flops(Mx, K, N) / (tb * 1e-6) / 1e12,
+                             "gbs": gemm_bytes(Mx, K, N) / (tb * 1e-6) / 1e9}
+                lin[name]["hbm_frac"] = lin[name]["gbs"] / HBM_PEAK_GBS
+                lin[name]["mfma_frac"] = lin[name]["tflops"] / MFMA_BF16_PEAK_TFS
+            tot_b = sum(row["bi"].values())
+            tot_f = sum(row["fast"].values())
+            byt = sum(gemm_bytes(Mx, K, N) for _, K, N in LINEARS)
+            per[str(Mx)] = {"linears": lin, "step_us": tot_b, "fast_step_us": tot_f,
+                            "overhead_pct": (tot_b / tot_f - 1) * 100,
+                            "gbs": byt / (tot_b * 1e-6) / 1e9,
+                            "hbm_frac": byt / (tot_b * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        extras["by_M"] = per
+        # bitwise invariance on this data: rows at M=1 vs rows in the batch
+        mism = 0
+        for name, K, N in LINEARS:
+            y_full = bi.gemm(acts[name], wsets[0][name])
+            for r in (0, M // 2, M - 1):
+                y1 = bi.gemm(acts[name][r:r + 1].contiguous(), wsets[0][name])
+                mism += int((y1.view(torch.int16) != y_full[r:r + 1].view(torch.int16)).sum())
+        extras["mismatches_m1_vs_batch"] = mism
+        extras["rmsnorm"] = bench_rmsnorm(torch, bi, synth, dev, args)
+        extras["attention"] = bench_attn(torch, bi, synth, dev, args)
+        result["extras"] = extras
+
+    if not args.no_cpu_baseline:
+        import oracle
+        result["cpu_baseline"] = cpu_baseline(synth, oracle, M)
+    print(json.dumps(result))
+
+
+def bench_rmsnorm(torch, bi, synth, dev, args):
+    M, H = 512, 4096
+    xs = [synth.rmsnorm_inputs(M, H, seed=50 + i, device=dev) for i in range(8)]
+    y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    res = {}
+    for name, fn in (("bi", bi.rmsnorm), ("fast", bi.rmsnorm_fast)):
+        for i in range(3):
+            fn(xs[i % 8][0], xs[i % 8][1], out=y)
+        torch.cuda.synchronize()
+        t = Timer(torch)
+        for i in range(50):
+            e = t.start()
+            fn(xs[i % 8][0], xs[i % 8][1], out=y)
+            t.stop(e)
+        torch.cuda.synchronize()
+        res[name] = t.mean_ms() * 1e3
+    byt = 4.0 * M * H + 2 * H
+    return {"M": M, "H": H, "us": res["bi"], "fast_us": res["fast"],
+            "overhead_pct": (res["bi"] / res["fast"] - 1) * 100,
+            "gbs": byt / (res["bi"] * 1e-6) / 1e9, "hbm_frac": byt / (res["bi"] * 1e-6) / 1e12 * 1e3 / HBM_PEAK_GBS}
+
+
+def bench_attn(torch, bi, synth, dev, args):
+    import numpy as np
+    B = 64
+    ctx = synth.ctx_lens_uniform(B, seed=3)
+    q, kv, bt, cl = synth.attn_inputs(ctx, seed=3, device=dev)
+    btd = torch.from_numpy(bt).to(dev)
+    cld = torch.from_numpy(cl).to(dev)
+    mc = int(ctx.max())
+    out = torch.empty_like(q)
+    res = {}
+    for name, fn in (("bi", bi.paged_decode_attn), ("fast", bi.paged_decode_attn_fast)):
+        for _ in range(2):
+            fn(q, kv, btd, cld, max_ctx_len=mc, out=out)
+        torch.cuda.synchronize()
+        t = Timer(torch)
+        for _ in range(10):
+            e = t.start()
+            fn(q, kv, btd, cld, max_ctx_len=mc, out=out)
+            t.stop(e)
+        torch.cuda.synchronize()
+        res[name] = t.mean_ms() * 1e3
+    tokens = int(np.sum(ctx))
+    byt = tokens * 8 * 128 * 2 * 2 + 2 * B * 32 * 128 * 2 + 4 * int(np.sum((ctx + 15) // 16))
+    return {"B": B, "mean_ctx": float(np.mean(ctx)), "us": res["bi"], "fast_us": res["fast"],
+            "overhead_pct": (res["bi"] / res["fast"] - 1) * 100,
+            "gbs": byt / (res["bi"] * 1e-6) / 1e9,
+            "hbm_frac": byt / (res["bi"] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+// bi_api.hip -- the extern "C" entry points declared in include/bi.h:
+// argument checks, workspace sizing, status codes and version string.
+// Every check happens before anything is enqueued.
+#include <stdio.h>
+
+#include "bi_internal.h"
+
+#ifndef BI_GIT_SHA
+#define BI_GIT_SHA "unknown"
+#endif
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// CU count of the current device, read once per device; only the fast twins
+// use it (the batch-invariant entry points never look at it).
+int current_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int check_gemm(const void* x, const void* W, const void* y, int64_t M, int64_t N, int64_t K) {
+  if (!x || !W || !y) return BI_ERR_NULL;
+  if (M <= 0 || N <= 0 || K <= 0) return BI_ERR_SHAPE;
+  if (M >= kMaxElems || N >= kMaxElems || K >= kMaxElems) return BI_ERR_SHAPE;
+  if (M * K >= kMaxElems || K * N >= kMaxElems || M * N >= kMaxElems) return BI_ERR_SHAPE;
+  if (K % 32 != 0 || N % 64 != 0) return BI_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(W) || !aligned16(y)) return BI_ERR_UNSUPPORTED;
+  return BI_OK;
+}
+
+int check_rms(const void* x, const void* g, const void* y, int64_t M, int64_t H) {
+  if (!x || !g || !y) return BI_ERR_NULL;
+  if (M <= 0 || H <= 0 || M >= kMaxElems || H >= kMaxElems || M * H >= kMaxElems)
+    return BI_ERR_SHAPE;
+  if (H % 8 != 0) return BI_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(g) || !aligned16(y)) return BI_ERR_UNSUPPORTED;
+  return BI_OK;
+}
+
+int check_attn(const void* q, const void* kv, const void* bt, const void* cl, const void* out,
+               const bi_attn_desc* d) {
+  if (!q || !kv || !bt || !cl || !out || !d) return BI_ERR_NULL;
+  if (d->batch <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
+      d->page_size <= 0 || d->max_blocks_per_seq <= 0 || d->num_pages <= 0 || d->max_ctx_len <= 0)
+    return BI_ERR_SHAPE;
+  if ((int64_t)d->max_ctx_len > (int64_t)d->max_blocks_per_seq * d->page_size) return BI_ERR_SHAPE;
+  if ((int64_t)d->batch * d->max_blocks_per_seq >= kMaxElems) return BI_ERR_SHAPE;
+  if (d->head_dim != 128 || d->page_size != 16) return BI_ERR_UNSUPPORTED;
+  if (d->num_q_heads % d->num_kv_heads != 0) return BI_ERR_UNSUPPORTED;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return BI_ERR_UNSUPPORTED;
+  if (!(d->scale == d->scale)) return BI_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || ((uintptr_t)bt & 3u) ||
+      ((uintptr_t)cl & 3u))
+    return BI_ERR_UNSUPPORTED;
+  return BI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bi_version(void) {
+  static char buf[512];
+  static int done = 0;
+  if (!done) {
+    snprintf(buf, sizeof buf,
+             "libbi 0.1.0 git=%s hip=%d.%d target=gfx950 "
+             "gemm: mfma_f32_16x16x32_bf16 KB=%d KC=%d fold=left split_maxM=64 tile=128x128; "
+             "rmsnorm: lanes=%d vec=8 butterfly=32..1 waves=((0+1)+2)+3 sqrt/div=IEEE; "
+             "attn: chunk=%d tile=%d combine=chunk-order exp=__expf",
+             BI_GIT_SHA, HIP_VERSION_MAJOR, HIP_VERSION_MINOR, bi::SCHED_GEMM_KB, bi::SCHED_GEMM_KC,
+             bi::SCHED_RMS_LANES, bi::SCHED_ATTN_CHUNK, bi::SCHED_ATTN_TILE);
+    done = 1;
+  }
+  return buf;
+}
+
+const char* bi_status_string(int status) {
+  switch (status) {
+    case BI_OK: return "ok";
+    case BI_ERR_NULL: return "null pointer";
+    case BI_ERR_SHAPE: return "bad shape";
+    case BI_ERR_UNSUPPORTED: return "unsupported shape or alignment";
+    case BI_ERR_WORKSPACE: return "workspace too small";
+    case BI_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t bi_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return bi::gemm_ws_bytes(M, N, K, false, 0);
+}
+
+size_t bi_gemm_fast_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return bi::gemm_ws_bytes(M, N, K, true, current_cus());
+}
+
+static int gemm_entry(const bi_bf16* x, const bi_bf16* W, bi_bf16* y, int64_t M, int64_t N,
+                      int64_t K, void* ws, size_t ws_bytes, void* stream, bool fast) {
+  int st = check_gemm(x, W, y, M, N, K);
+  if (st != BI_OK) return st;
+  const int cus = fast ? current_cus() : 0;
+  const size_t need = bi::gemm_ws_bytes(M, N, K, fast, cus);
+  if (need > 0 && (!ws || ws_bytes < need)) return BI_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return BI_ERR_UNSUPPORTED;
+  return bi::launch_gemm(x, W, y, M, N, K, ws, ws_bytes, (hipStream_t)stream, fast, cus);
+}
+
+int bi_gemm(const bi_bf16* x, const bi_bf16* W, bi_bf16* y, int64_t M, int64_t N, int64_t K,
+            void* ws, size_t ws_bytes, void* stream) {
+  return gemm_entry(x, W, y, M, N, K, ws, ws_bytes, stream, false);
+}
+
+int bi_gemm_fast(const bi_bf16* x, const bi_bf16* W, bi_bf16* y, int64_t M, int64_t N, int64_t K,
+                 void* ws, size_t ws_bytes, void* stream) {
+  return gemm_entry(x, W, y, M, N, K, ws, ws_bytes, stream, true);
+}
+
+int bi_rmsnorm(const bi_bf16* x, const bi_bf16* g, bi_bf16* y, int64_t M, int64_t H, float eps,
+               void* stream) {
+  int st = check_rms(x, g, y, M, H);
+  if (st != BI_OK) return st;
+  return bi::launch_rmsnorm(x, g, y, M, H, eps, (hipStream_t)stream, false);
+}
+
+int bi_rmsnorm_fast(const bi_bf16* x, const bi_bf16* g, bi_bf16* y, int64_t M, int64_t H,
+                    float eps, void* stream) {
+  int st = check_rms(x, g, y, M, H);
+  if (st != BI_OK) return st;
+  return bi::launch_rmsnorm(x, g, y, M, H, eps, (hipStream_t)stream, true);
+}
+
+size_t bi_attn_workspace_bytes(const bi_attn_desc* d) {
+  if (!d || d->batch <= 0 || d->num_q_heads <= 0 || d->max_ctx_len <= 0) return 0;
+  return bi::attn_ws_bytes(d, false, 0);
+}
+
+size_t bi_attn_fast_workspace_bytes(const bi_attn_desc* d) {
+  if (!d || d->batch <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->max_ctx_len <= 0)
+    return 0;
+  return bi::attn_ws_bytes(d, true, current_cus());
+}
+
+static int attn_entry(const bi_bf16* q, const bi_bf16* kv, const int32_t* bt, const int32_t* cl,
+                      bi_bf16* out, const bi_attn_desc* d, void* ws, size_t ws_bytes,
+                      void* stream, bool fast) {
+  int st = check_attn(q, kv, bt, cl, out, d);
+  if (st != BI_OK) return st;
+  const int cus = fast ? current_cus() : 0;
+  const size_t need = bi::attn_ws_bytes(d, fast, cus);
+  if (!ws || ws_bytes < need) return BI_ERR_WORKSPACE;
+  if (!aligned16(ws)) return BI_ERR_UNSUPPORTED;
+  return bi::launch_attn(q, kv, bt, cl, out, d, ws, ws_bytes, (hipStream_t)stream, fast, cus);
+}
+
+int bi_paged_decode_attn(const bi_bf16* q, const bi_bf16* kv_pages, const int32_t* block_table,
+                         const int32_t* ctx_lens, bi_bf16* out, const bi_attn_desc* d, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return attn_entry(q, kv_pages, block_table, ctx_lens, out, d, ws, ws_bytes, stream, false);
+}
+
+int bi_paged_decode_attn_fast(const bi_bf16* q, const bi_bf16* kv_pages,
+                              const int32_t* block_table, const int32_t* ctx_lens, bi_bf16* out,
+                              const bi_attn_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  return attn_entry(q, kv_pages, block_table, ctx_lens, out, d, ws, ws_bytes, stream, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,276 @@
+// bi_attn.hip -- paged GQA decode attention, one query token per request.
+//
+//   out[b,h,:] = softmax_t(scale * q[b,h,:] . k_t) . v_t,  t < ctx_lens[b],
+//   kv head of q head h = h / G, G = num_q_heads / num_kv_heads.
+//
+// The Vosti abstract asks for outputs that do not move with the batch or the
+// paged KV layout; the Determinism article (section 4) fixes every split by
+// the data and combines partials in a fixed order.  Schedule of the
+// batch-invariant entry point, fixed by nothing but the token positions:
+//   chunk c = tokens [256c, 256c + 256) of the request, one workgroup per
+//   (chunk, kv head, request); inside it, tiles of 64 tokens in order with an
+//   online softmax per q head:
+//     s_t   = (sum_d q_d k_td, left to right) * scale
+//     m'    = max(m, max_t s_t);  alpha = exp(m - m') (0 while m = -inf)
+//     l     = l * alpha, then l = l + p_t in token order, p_t = exp(s_t - m')
+//     acc_d = acc_d * alpha, then acc_d = fma(p_t, v_td, acc_d) in token order
+//   the chunk's (m, l, acc[128]) go to an fp32 workspace;
+//   a combine kernel folds the chunks of each (request, head) in chunk order:
+//     M* = max_c m_c, w_c = exp(m_c - M*), Lsum = fma(l_c, w_c, Lsum),
+//     O_d = fma(acc_cd, w_c, O_d), out_d = bf16(O_d / Lsum).
+// Which page a token sits in only changes the address it is read from.
+//
+// The fast twin runs the same kernels with a chunk length picked per
+// request from the number of splits that fills the chip for this batch
+// (flash-decoding style), so its bits depend on the batch.
+#include "bi_common.h"
+#include "bi_internal.h"
+
+namespace bi {
+
+static constexpr int AD = 128;        // head_dim
+static constexpr int APS = 16;        // page size
+static constexpr int ATILE = 64;      // tokens per tile
+static constexpr int ACHUNK = 256;    // tokens per chunk (batch-invariant entry point)
+static constexpr int APART = AD + 4;  // floats per partial: m, l, 2 pad, acc[128]
+static constexpr int AKLD = AD + 8;   // padded K row in LDS (elements)
+
+// Chunk length for request length L: fixed, or (fast twin) from the split count.
+__device__ __forceinline__ int chunk_len(int L, int fixed_chunk, int splits) {
+  if (fixed_chunk > 0) return fixed_chunk;
+  const int per = (L + splits - 1) / splits;
+  return ((per + ATILE - 1) / ATILE) * ATILE;
+}
+
+// grid = (max chunks, num_kv_heads, batch), block = 256 (4 waves).
+// Wave w owns q heads w and w + 4 of the group (G <= 8): lane = token in the
+// score phase, lane = pair of dims (2 lane, 2 lane + 1) in the PV phase.
+template <int G>
+__global__ __launch_bounds__(256) void attn_chunk_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
+    float* __restrict__ part, int Hq, int Hkv, int max_blocks, long long num_pages, int max_ctx,
+    int nc_stride, int fixed_chunk, int splits, float scale) {
+  __shared__ __attribute__((aligned(16))) float qs[G][AD];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[ATILE * AKLD];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[ATILE * AD];
+  __shared__ __attribute__((aligned(16))) float ps[G][ATILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int b = blockIdx.z;
+  const int L = min((int)ctx_lens[b], max_ctx);
+  if (L <= 0) return;
+  const int C = chunk_len(L, fixed_chunk, splits);
+  const int nc = (L + C - 1) / C;
+  if (c >= nc) return;
+  const int t_begin = c * C;
+  const int t_end = min(L, t_begin + C);
+  const int32_t* bt = block_table + (size_t)b * max_blocks;
+
+  // q of this kv head's G query heads, widened to fp32.
+  for (int i = tid; i < G * AD; i += 256)
+    qs[i / AD][i % AD] = bf16_to_f32(q[((size_t)b * Hq + hk * G) * AD + i]);
+
+  // K/V tile loader: 64 tokens x 16 chunks of 16 B for each of K and V;
+  // chunk ci = tid + 256 i: token ci/16, dims 8*(ci%16)..+7.
+  u32x4_t kr[4], vr[4];
+  auto load_tile = [&](int t0, int nt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = tid + 256 * i;
+      const int tt = ci >> 4;
+      const int dc = ci & 15;
+      kr[i] = u32x4_t{0u, 0u, 0u, 0u};
+      vr[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (tt < nt) {
+        const int t = t0 + tt;
+        const long long page = bt[t / APS];
+        if (page >= 0 && page < num_pages) {
+          const size_t kofs = (((size_t)page * 2 + 0) * Hkv + hk) * (APS * AD) + (t % APS) * AD + dc * 8;
+          const size_t vofs = kofs + (size_t)Hkv * APS * AD;
+          kr[i] = ldg128(kv + kofs);
+          vr[i] = ldg128(kv + vofs);
+        }
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = tid + 256 * i;
+      const int tt = ci >> 4;
+      const int dc = ci & 15;
+      *(u32x4_t*)&ks[tt * AKLD + dc * 8] = kr[i];
+      *(u32x4_t*)&vs[tt * AD + dc * 8] = vr[i];
+    }
+  };
+
+  constexpr int HPW = (G + 3) / 4;  // heads per wave
+  float m[HPW], l[HPW], acc0[HPW], acc1[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.0f;
+    acc0[j] = 0.0f;
+    acc1[j] = 0.0f;
+  }
+
+  int nt = min(ATILE, t_end - t_begin);
+  load_tile(t_begin, nt);
+  for (int t0 = t_begin; t0 < t_end; t0 += ATILE) {
+    nt = min(ATILE, t_end - t0);
+    __syncthreads();  // previous tile fully consumed (and q staged)
+    store_tile();
+    __syncthreads();
+    const int t1 = t0 + ATILE;
+    if (t1 < t_end) load_tile(t1, min(ATILE, t_end - t1));
+
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const int hh = wave + 4 * j;
+      if (hh < G) {
+        // scores: lane = token
+        float s = -INFINITY;
+        if (lane < nt) {
+          float dot = 0.0f;
+          const uint16_t* krow = ks + lane * AKLD;
+#pragma unroll 4
+          for (int d0 = 0; d0 < AD; d0 += 8) {
+            const u32x4_t kv8 = *(const u32x4_t*)(krow + d0);
+            const f32x4_t qa = *(const f32x4_t*)&qs[hh][d0];
+            const f32x4_t qb = *(const f32x4_t*)&qs[hh][d0 + 4];
+            dot = dot + qa[0] * bf16_lo(kv8[0]);
+            dot = dot + qa[1] * bf16_hi(kv8[0]);
+            dot = dot + qa[2] * bf16_lo(kv8[1]);
+            dot = dot + qa[3] * bf16_hi(kv8[1]);
+            dot = dot + qb[0] * bf16_lo(kv8[2]);
+            dot = dot + qb[1] * bf16_hi(kv8[2]);
+            dot = dot + qb[2] * bf16_lo(kv8[3]);
+            dot = dot + qb[3] * bf16_hi(kv8[3]);
+          }
+          s = dot * scale;
+        }
+        float mt = s;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));
+        const float mn = fmaxf(m[j], mt);
+        const float alpha = (m[j] == -INFINITY) ? 0.0f : __expf(m[j] - mn);
+        ps[hh][lane] = (lane < nt) ? __expf(s - mn) : 0.0f;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        // l and acc: every lane walks the tokens in order
+        float lj = l[j] * alpha;
+        float a0 = acc0[j] * alpha;
+        float a1 = acc1[j] * alpha;
+        const uint32_t* vcol = (const uint32_t*)vs + lane;  // dims 2 lane, 2 lane + 1
+        for (int i = 0; i < nt; ++i) {
+          const float p = ps[hh][i];
+          const uint32_t v2 = vcol[i * (AD / 2)];
+          lj = lj + p;
+          a0 = __fmaf_rn(p, bf16_lo(v2), a0);
+          a1 = __fmaf_rn(p, bf16_hi(v2), a1);
+        }
+        l[j] = lj;
+        acc0[j] = a0;
+        acc1[j] = a1;
+        m[j] = mn;
+      }
+    }
+  }
+
+  // chunk partial: [b][h][c][m, l, -, -, acc[128]]
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    const int hh = wave + 4 * j;
+    if (hh < G) {
+      float* pp = part + (((size_t)b * Hq + hk * G + hh) * nc_stride + c) * APART;
+      if (lane == 0) {
+        pp[0] = m[j];
+        pp[1] = l[j];
+      }
+      pp[4 + 2 * lane] = acc0[j];
+      pp[5 + 2 * lane] = acc1[j];
+    }
+  }
+}
+
+// grid = (num_q_heads, batch), block = 128 (one lane per dim).
+__global__ __launch_bounds__(128) void attn_combine_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ ctx_lens,
+    uint16_t* __restrict__ out, int Hq, int max_ctx, int nc_stride, int fixed_chunk, int splits) {
+  const int d = threadIdx.x;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  uint16_t* o = out + ((size_t)b * Hq + h) * AD;
+  const int L = min((int)ctx_lens[b], max_ctx);
+  if (L <= 0) {
+    o[d] = 0;
+    return;
+  }
+  const int C = chunk_len(L, fixed_chunk, splits);
+  const int nc = (L + C - 1) / C;
+  const float* pp = part + ((size_t)b * Hq + h) * nc_stride * APART;
+  float mx = -INFINITY;
+  for (int c = 0; c < nc; ++c) mx = fmaxf(mx, pp[c * APART]);
+  float ls = 0.0f, acc = 0.0f;
+  for (int c = 0; c < nc; ++c) {
+    const float w = __expf(pp[c * APART] - mx);
+    ls = __fmaf_rn(pp[c * APART + 1], w, ls);
+    acc = __fmaf_rn(pp[c * APART + 4 + d], w, acc);
+  }
+  o[d] = (uint16_t)f32_to_bf16_bits(acc / ls);  // IEEE division
+}
+
+static int attn_splits(const bi_attn_desc* d, int num_cus) {
+  const long long units = (long long)d->batch * d->num_kv_heads;
+  long long s = (4LL * num_cus + units - 1) / units;
+  const long long maxs = (d->max_ctx_len + ATILE - 1) / ATILE;
+  s = std::max(1LL, std::min(s, maxs));
+  return (int)s;
+}
+
+static int nc_stride_of(const bi_attn_desc* d, bool fast, int num_cus) {
+  return fast ? attn_splits(d, num_cus) : (d->max_ctx_len + ACHUNK - 1) / ACHUNK;
+}
+
+size_t attn_ws_bytes(const bi_attn_desc* d, bool fast, int num_cus) {
+  const size_t nc = (size_t)nc_stride_of(d, fast, num_cus);
+  return WS_COUNTER_BYTES + (size_t)d->batch * d->num_q_heads * nc * APART * sizeof(float);
+}
+
+int launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* block_table,
+                const int32_t* ctx_lens, uint16_t* out, const bi_attn_desc* d, void* ws,
+                size_t ws_bytes, hipStream_t stream, bool fast, int num_cus) {
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const int ncs = nc_stride_of(d, fast, num_cus);
+  if (ws_bytes < attn_ws_bytes(d, fast, num_cus)) return BI_ERR_WORKSPACE;
+  if (ncs > 65535 || d->num_kv_heads > 65535 || d->batch > 65535) return BI_ERR_UNSUPPORTED;
+  float* part = (float*)((char*)ws + WS_COUNTER_BYTES);
+  const int fixed = fast ? 0 : ACHUNK;
+  const int splits = fast ? ncs : 0;
+  dim3 grid((unsigned)ncs, (unsigned)d->num_kv_heads, (unsigned)d->batch);
+#define BI_ATTN_LAUNCH(GG)                                                                    \
+  hipLaunchKernelGGL(attn_chunk_kernel<GG>, grid, dim3(256), 0, stream, q, kv, block_table,  \
+                     ctx_lens, part, d->num_q_heads, d->num_kv_heads, d->max_blocks_per_seq, \
+                     (long long)d->num_pages, d->max_ctx_len, ncs, fixed, splits, d->scale)
+  switch (G) {
+    case 1: BI_ATTN_LAUNCH(1); break;
+    case 2: BI_ATTN_LAUNCH(2); break;
+    case 4: BI_ATTN_LAUNCH(4); break;
+    case 8: BI_ATTN_LAUNCH(8); break;
+    default: return BI_ERR_UNSUPPORTED;
+  }
+#undef BI_ATTN_LAUNCH
+  if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)d->num_q_heads, (unsigned)d->batch),
+                     dim3(128), 0, stream, part, ctx_lens, out, d->num_q_heads, d->max_ctx_len,
+                     ncs, fixed, splits);
+  return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+}  // namespace bi

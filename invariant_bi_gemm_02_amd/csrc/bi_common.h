@@ -1,0 +1,55 @@
+// bi_common.h -- device helpers shared by the HIP kernels of libbi.so.
+// gfx950 (CDNA4) only: wave64, v_mfma_f32_16x16x32_bf16, ds_read_b64_tr_b16.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bi {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define BI_LDS __attribute__((address_space(3)))
+
+// bf16 bits -> fp32: exact (bf16 is the top half of binary32).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0u) return (u >> 16) | 0x0040u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// One matrix-core op: c += a(16x32) . b(32x16), bf16 in, fp32 accumulate.
+// Operand layout on gfx950, lane l of the wave:
+//   a: row l%16 of A, k = (l/16)*8 .. +7;   b: column l%16 of B, same k;
+//   c: column l%16 of C, rows (l/16)*4 .. +3.
+__device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// LDS transpose read of 16-bit data.  Within each group of 16 lanes, lane
+// 4r + c passes the address of 4 consecutive elements (row r, columns
+// 4c..4c+3) of a 4x16 block; afterwards lane i of the group holds column i
+// of the block, rows 0..3.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* lds_addr) {
+  i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BI_LDS i16x4_t*)(lds_addr));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+__device__ __forceinline__ u32x4_t ldg128(const void* p) { return *(const u32x4_t*)p; }
+__device__ __forceinline__ void stg128(void* p, const u32x4_t& v) { *(u32x4_t*)p = v; }
+
+}  // namespace bi

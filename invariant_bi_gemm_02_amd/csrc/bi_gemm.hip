@@ -1,0 +1,405 @@
+// bi_gemm.hip -- y[M,N] = bf16(x[M,K] . W[K,N]) on the gfx950 matrix cores.
+//
+// Reduction schedule of the batch-invariant entry point (fixed by K alone):
+//   K-block  = 32 = one v_mfma_f32_16x16x32_bf16,
+//   segment  = KC = 512 consecutive K (16 blocks), accumulated from +0,
+//   segments folded left to right 0..S-1 with fp32 adds, S = ceil(K/KC),
+//   one round-to-nearest-even narrowing to bf16.
+// This is the two-stage deterministic reduction of the Determinism article
+// (section 4): per-slice partial sums written to a fixed workspace and added
+// in the fixed index order, with no float atomics anywhere; the K split is
+// the same whatever M is, and the M tile is padded rather than re-chosen.
+//
+// Two kernels implement that schedule; which one runs depends on M, and the
+// bits never do (both issue the same matrix-core instruction on the same
+// operands in the same order, start every segment from +0, and fold the
+// segments with the same fp32 adds):
+//   gemm_split_kernel  small M (weight streaming, HBM bound): one workgroup
+//                      per (64-column tile, segment, 64-row tile); segment
+//                      sums go to an fp32 workspace; the last workgroup of a
+//                      tile to arrive (integer ticket) folds them in order.
+//   gemm_tile_kernel   large M (matrix-core bound): 128x128 output tiles, all
+//                      segments of K in one workgroup, folded in registers.
+// Padding rows (>= M) load as zero, are never stored, and 16-row sub-tiles
+// that are entirely padding skip their matrix-core ops.
+//
+// W is [K,N] row-major (N contiguous), while the matrix core wants 8
+// consecutive K per lane for the B operand.  W tiles are therefore staged in
+// LDS as they sit in memory and read back with the LDS transpose read
+// (ds_read_b64_tr_b16), which hands each lane one column.
+//
+// The fast twin reuses both kernels with a schedule picked from M and the CU
+// count: the split kernel with a K slice sized to fill the chip, and the tile
+// kernel with a single accumulation chain over all of K (no segments).
+#include "bi_common.h"
+#include "bi_internal.h"
+
+namespace bi {
+
+static constexpr int KB = 32;        // K per matrix-core op
+static constexpr int SPLIT_BN = 64;  // columns per split workgroup (4 waves x 16)
+static constexpr int SPLIT_BM = 64;  // rows per split workgroup (4 sub-tiles of 16)
+static constexpr int SPLIT_SK = 128; // K rows of W staged per LDS buffer
+static constexpr int SPLIT_LDW = SPLIT_BN + 16;  // padded LDS row (elements)
+
+// ---------------------------------------------------------------------------
+// Split kernel (small M)
+// ---------------------------------------------------------------------------
+// grid = (N/64, S, ceil(M/64)), block = 256 (4 waves).  Wave w owns columns
+// n0 + 16w .. +15 of the tile and every 16-row sub-tile that holds a row < M.
+// Per stage of 128 K: the W slab (128 x 64) goes through LDS, the x
+// fragments stay in registers; the next stage is fetched while this one runs.
+// MAXSUB = 1 for M <= 16 (fewer registers), 4 otherwise.
+template <int MAXSUB>
+__global__ __launch_bounds__(256) void gemm_split_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, uint16_t* __restrict__ y,
+    float* __restrict__ part, int* __restrict__ counters, int M, int N, int K, int KC, int S) {
+  __shared__ __attribute__((aligned(16))) uint16_t wl[2][SPLIT_SK * SPLIT_LDW];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ntile = blockIdx.x;
+  const int seg = blockIdx.y;
+  const int mtile = blockIdx.z;
+  const int n0 = ntile * SPLIT_BN;
+  const int m0 = mtile * SPLIT_BM;
+  const int k_begin = seg * KC;
+  const int k_end = min(K, k_begin + KC);
+  const int rows = min(SPLIT_BM, M - m0);
+  const int nsub = min(MAXSUB, (rows + 15) >> 4);  // 16-row sub-tiles holding a real row
+
+  // A operand lanes: row m0 + 16*sub + lane%16, k = kb + (lane/16)*8 .. +7.
+  const int arow = lane & 15;
+  const int g = lane >> 4;
+  // B operand via transpose read: lane 4r+c of group g addresses row
+  // kb + 8g + 4h + r, columns 16*wave + 4c .. +3, for h = 0, 1.
+  const int tr_r = (lane & 15) >> 2;
+  const int tr_c = lane & 3;
+
+  u32x4_t wreg[4];
+  u32x4_t acur[MAXSUB][4], anext[MAXSUB][4];
+  // One stage: W rows k0..k0+127 (chunk c = tid + 256 i: row c/8, columns
+  // 8*(c%8)..+7) and the x fragments of its four K-blocks.
+  auto load_stage = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int k = k0 + (c >> 3);
+      wreg[i] = (k < k_end) ? ldg128(W + (size_t)k * N + n0 + (c & 7) * 8)
+                            : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int s = 0; s < MAXSUB; ++s) {
+      const int m = m0 + s * 16 + arow;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kb = k0 + j * KB;
+        anext[s][j] = (s < nsub && m < M && kb < k_end) ? ldg128(x + (size_t)m * K + kb + g * 8)
+                                                         : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_w = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      *(u32x4_t*)&wl[buf][(c >> 3) * SPLIT_LDW + (c & 7) * 8] = wreg[i];
+    }
+  };
+
+  f32x4_t acc[MAXSUB];
+#pragma unroll
+  for (int s = 0; s < MAXSUB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nstage = (k_end - k_begin + SPLIT_SK - 1) / SPLIT_SK;
+  load_stage(k_begin);
+  store_w(0);
+#pragma unroll
+  for (int s = 0; s < MAXSUB; ++s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acur[s][j] = anext[s][j];
+  __syncthreads();
+  for (int st = 0; st < nstage; ++st) {
+    const int k0 = k_begin + st * SPLIT_SK;
+    if (st + 1 < nstage) load_stage(k0 + SPLIT_SK);
+    const uint16_t* wb = wl[st & 1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (k0 + j * KB < k_end) {
+        const uint16_t* base = wb + (j * KB + 8 * g + tr_r) * SPLIT_LDW + 16 * wave + 4 * tr_c;
+        const u32x2_t b0 = lds_read_tr16(base);
+        const u32x2_t b1 = lds_read_tr16(base + 4 * SPLIT_LDW);
+        const u32x4_t bfrag = u32x4_t{b0.x, b0.y, b1.x, b1.y};
+#pragma unroll
+        for (int s = 0; s < MAXSUB; ++s)
+          if (s < nsub) acc[s] = mfma16x16x32(acur[s][j], bfrag, acc[s]);
+      }
+    }
+    if (st + 1 < nstage) {
+      store_w((st + 1) & 1);
+#pragma unroll
+      for (int s = 0; s < MAXSUB; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acur[s][j] = anext[s][j];
+    }
+    __syncthreads();
+  }
+
+  // Segment partial -> workspace part[seg][m][n] (rows < M only).
+  const int ccol = n0 + 16 * wave + (lane & 15);
+#pragma unroll
+  for (int s = 0; s < MAXSUB; ++s) {
+    if (s < nsub) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + s * 16 + g * 4 + e;
+        if (m < M) part[((size_t)seg * M + m) * N + ccol] = acc[s][e];
+      }
+    }
+  }
+
+  // Arrival ticket: the last workgroup of this (mtile, ntile) folds.  The
+  // ticket decides only which workgroup folds, never the order of the adds.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  int* ctr = counters + (size_t)mtile * gridDim.x + ntile;
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old == S - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+  // Fold the S segment partials left to right: y32 = p0; y32 = y32 + p_s.
+  const int col = n0 + (tid & 63);
+  for (int r = tid >> 6; r < rows; r += 4) {
+    const int m = m0 + r;
+    const float* p = part + (size_t)m * N + col;
+    float y32 = p[0];
+    for (int s = 1; s < S; ++s) y32 = y32 + p[(size_t)s * M * N];
+    y[(size_t)m * N + col] = (uint16_t)f32_to_bf16_bits(y32);
+  }
+  if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Tile kernel (large M)
+// ---------------------------------------------------------------------------
+static constexpr int TBM = 128, TBN = 128, TBK = 64;
+static constexpr int T_LDX = TBK + 8;    // padded x row in LDS (elements)
+static constexpr int T_LDW = TBN + 16;   // padded W row in LDS (elements)
+
+// grid = (N/128, ceil(M/128)), block = 256: waves in a 2x2 grid, 64x64 each.
+// FOLD: true  -> segments of KC from +0, folded in registers (invariant);
+//       false -> one accumulation chain over all of K (fast twin).
+template <bool FOLD>
+__global__ __launch_bounds__(256) void gemm_tile_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, uint16_t* __restrict__ y,
+    int M, int N, int K, int KC) {
+  __shared__ __attribute__((aligned(16))) uint16_t xl[2][TBM * T_LDX];
+  __shared__ __attribute__((aligned(16))) uint16_t wl[2][TBK * T_LDW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * TBN;
+  const int m0 = blockIdx.y * TBM;
+
+  // Loaders: x stage 128 rows x 64 K (8 chunks per row), W stage 64 rows x
+  // 128 columns (16 chunks per row); 4 chunks of 16 B per thread for each.
+  u32x4_t xr[4], wr[4];
+  auto load_stage = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c >> 3, kc = c & 7;
+      const int m = m0 + r;
+      if (m < M && k0 + kc * 8 < K)
+        xr[i] = ldg128(x + (size_t)m * K + k0 + kc * 8);
+      else
+        xr[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c >> 4, nc = c & 15;
+      const int k = k0 + r;
+      if (k < K && n0 + nc * 8 < N)
+        wr[i] = ldg128(W + (size_t)k * N + n0 + nc * 8);
+      else
+        wr[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      *(u32x4_t*)&xl[buf][(c >> 3) * T_LDX + (c & 7) * 8] = xr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      *(u32x4_t*)&wl[buf][(c >> 4) * T_LDW + (c & 15) * 8] = wr[i];
+    }
+  };
+
+  f32x4_t acc[4][4];
+  f32x4_t tot[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      tot[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // 16-row sub-tiles of this wave that hold at least one row < M.
+  const int wrow0 = m0 + wm * 64;
+  const int nsub = max(0, min(4, (M - wrow0 + 15) >> 4));
+
+  const int g = lane >> 4;
+  const int tr_r = (lane & 15) >> 2;
+  const int tr_c = lane & 3;
+  const int arow = lane & 15;
+
+  const int nstage = (K + TBK - 1) / TBK;
+  const int blocks_per_seg = KC / KB;
+  int seg = 0;
+  int kblk_in_seg = 0;
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int st = 0; st < nstage; ++st) {
+    const int k0 = st * TBK;
+    if (st + 1 < nstage) load_stage(k0 + TBK);
+    const uint16_t* xs = xl[st & 1];
+    const uint16_t* ws = wl[st & 1];
+    const int nkb = min(TBK, K - k0) / KB;
+    for (int j = 0; j < nkb; ++j) {
+      u32x4_t bf[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint16_t* base = ws + (j * KB + 8 * g + tr_r) * T_LDW + wn * 64 + t * 16 + 4 * tr_c;
+        const u32x2_t b0 = lds_read_tr16(base);
+        const u32x2_t b1 = lds_read_tr16(base + 4 * T_LDW);
+        bf[t] = u32x4_t{b0.x, b0.y, b1.x, b1.y};
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s < nsub) {
+          const u32x4_t af =
+              *(const u32x4_t*)&xs[(wm * 64 + s * 16 + arow) * T_LDX + j * KB + g * 8];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[s][t] = mfma16x16x32(af, bf[t], acc[s][t]);
+        }
+      }
+      if (FOLD) {
+        // segment boundary: fold this segment's sum into the running total
+        if (++kblk_in_seg == blocks_per_seg || (k0 + (j + 1) * KB) >= K) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              if (seg == 0)
+                tot[s][t] = acc[s][t];
+              else
+                tot[s][t] = tot[s][t] + acc[s][t];
+              acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+          ++seg;
+          kblk_in_seg = 0;
+        }
+      }
+    }
+    if (st + 1 < nstage) store_stage((st + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue: narrow and store rows < M.
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s < nsub) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int col = n0 + wn * 64 + t * 16 + (lane & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = wrow0 + s * 16 + (lane >> 4) * 4 + e;
+          const float v = FOLD ? tot[s][t][e] : acc[s][t][e];
+          if (m < M && col < N) y[(size_t)m * N + col] = (uint16_t)f32_to_bf16_bits(v);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+static constexpr int BI_KC = 512;  // invariant segment length
+static constexpr int SPLIT_MAX_M = 64;
+
+size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t S) {
+  return (size_t)S * (size_t)M * (size_t)N * sizeof(float);
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool fast, int num_cus) {
+  if (M > SPLIT_MAX_M) return 0;  // the tile kernel needs no workspace
+  int64_t S;
+  if (!fast) {
+    S = ceil_div(K, BI_KC);
+  } else {
+    const int64_t KC = fast_split_kc(M, N, K, num_cus);
+    S = ceil_div(K, KC);
+  }
+  return WS_COUNTER_BYTES + gemm_split_ws_bytes(M, N, S);
+}
+
+// K slice of the fast twin: enough slices to give ~2 workgroups per CU.
+int64_t fast_split_kc(int64_t M, int64_t N, int64_t K, int num_cus) {
+  const int64_t tiles = (N / SPLIT_BN) * ceil_div(M, SPLIT_BM);
+  int64_t splits = ceil_div(2 * (int64_t)num_cus, tiles);
+  splits = std::max<int64_t>(1, std::min<int64_t>(splits, K / KB));
+  int64_t kc = ceil_div(ceil_div(K, splits), KB) * KB;
+  return kc;
+}
+
+int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, int64_t N,
+                int64_t K, void* ws, size_t ws_bytes, hipStream_t stream, bool fast,
+                int num_cus) {
+  if (M <= SPLIT_MAX_M) {
+    const int64_t KC = fast ? fast_split_kc(M, N, K, num_cus) : BI_KC;
+    const int64_t S = ceil_div(K, KC);
+    const int64_t mt = ceil_div(M, SPLIT_BM), nt = N / SPLIT_BN;
+    if (mt * nt * (int64_t)sizeof(int) > WS_COUNTER_BYTES) return BI_ERR_UNSUPPORTED;
+    if (S > 65535) return BI_ERR_UNSUPPORTED;
+    if (ws_bytes < WS_COUNTER_BYTES + gemm_split_ws_bytes(M, N, S)) return BI_ERR_WORKSPACE;
+    int* counters = (int*)ws;
+    float* part = (float*)((char*)ws + WS_COUNTER_BYTES);
+    dim3 grid((unsigned)nt, (unsigned)S, (unsigned)mt);
+    if (M <= 16)
+      hipLaunchKernelGGL(gemm_split_kernel<1>, grid, dim3(256), 0, stream, x, W, y, part,
+                         counters, (int)M, (int)N, (int)K, (int)KC, (int)S);
+    else
+      hipLaunchKernelGGL(gemm_split_kernel<4>, grid, dim3(256), 0, stream, x, W, y, part,
+                         counters, (int)M, (int)N, (int)K, (int)KC, (int)S);
+  } else {
+    dim3 grid((unsigned)ceil_div(N, TBN), (unsigned)ceil_div(M, TBM));
+    if (fast)
+      hipLaunchKernelGGL(gemm_tile_kernel<false>, grid, dim3(256), 0, stream, x, W, y, (int)M,
+                         (int)N, (int)K, (int)K);
+    else
+      hipLaunchKernelGGL(gemm_tile_kernel<true>, grid, dim3(256), 0, stream, x, W, y, (int)M,
+                         (int)N, (int)K, BI_KC);
+  }
+  return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+}  // namespace bi

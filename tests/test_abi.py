@@ -1,0 +1,114 @@
+"""The C-ABI library loads, exports every symbol include/bi.h declares, and
+rejects bad arguments before touching the GPU (these calls never reach a
+launch, so they run without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_bi_gemm_02_amd as bi
+from invariant_bi_gemm_02_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bi.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bi_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libbi.so is not built (run __graft_entry__.build())")
+    return bi.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in bi.h but not exported"
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_version_names_target_and_schedule(lib):
+    v = bi.version()
+    assert "gfx950" in v and "KC=512" in v and "chunk=256" in v
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.bi_status_string(code)
+
+
+def P(v):
+    return ctypes.c_void_p(v)
+
+
+def test_gemm_argument_checks(lib):
+    ok = 0x1000
+    assert lib.bi_gemm(None, P(ok), P(ok), 1, 64, 32, None, 0, None) == -1
+    assert lib.bi_gemm(P(ok), P(ok), P(ok), 0, 64, 32, None, 0, None) == -2
+    assert lib.bi_gemm(P(ok), P(ok), P(ok), 1, 64, 33, None, 0, None) == -3   # K % 32
+    assert lib.bi_gemm(P(ok), P(ok), P(ok), 1, 48, 32, None, 0, None) == -3   # N % 64
+    assert lib.bi_gemm(P(ok + 2), P(ok), P(ok), 1, 64, 32, None, 0, None) == -3  # alignment
+    assert lib.bi_gemm(P(ok), P(ok), P(ok), 1 << 20, 1 << 12, 1 << 12, None, 0, None) == -2
+    # small M needs the split workspace
+    need = lib.bi_gemm_workspace_bytes(1, 4096, 4096)
+    assert need >= 65536 + 8 * 4096 * 4
+    assert lib.bi_gemm(P(ok), P(ok), P(ok), 1, 4096, 4096, P(ok), need - 16, None) == -4
+    assert lib.bi_gemm(P(ok), P(ok), P(ok), 1, 4096, 4096, None, 0, None) == -4
+    # large M uses no workspace
+    assert lib.bi_gemm_workspace_bytes(2048, 4096, 4096) == 0
+
+
+def test_workspace_size_depends_on_k_only_through_segments(lib):
+    a = lib.bi_gemm_workspace_bytes(16, 4096, 4096)
+    b = lib.bi_gemm_workspace_bytes(16, 4096, 14336)
+    assert a == 65536 + 8 * 16 * 4096 * 4
+    assert b == 65536 + 28 * 16 * 4096 * 4
+
+
+def test_rmsnorm_argument_checks(lib):
+    ok = 0x1000
+    f = ctypes.c_float(1e-5)
+    assert lib.bi_rmsnorm(None, P(ok), P(ok), 1, 4096, f, None) == -1
+    assert lib.bi_rmsnorm(P(ok), P(ok), P(ok), 1, 0, f, None) == -2
+    assert lib.bi_rmsnorm(P(ok), P(ok), P(ok), 1, 4100, f, None) == -3
+    assert lib.bi_rmsnorm_fast(P(ok), P(ok), P(ok), -1, 4096, f, None) == -2
+
+
+def test_attention_argument_checks(lib):
+    ok = 0x1000
+    d = _lib.AttnDesc(4, 32, 8, 128, 16, 64, 1000, 1024, 0.088)
+    args = [P(ok), P(ok), P(ok), P(ok), P(ok)]
+    need = lib.bi_attn_workspace_bytes(ctypes.byref(d))
+    assert need == 65536 + 4 * 32 * 4 * 132 * 4
+    assert lib.bi_paged_decode_attn(*args, ctypes.byref(d), P(ok), need - 4, None) == -4
+    bad = _lib.AttnDesc(4, 32, 8, 64, 16, 64, 1000, 1024, 0.088)       # head_dim 64
+    assert lib.bi_paged_decode_attn(*args, ctypes.byref(bad), P(ok), 1 << 30, None) == -3
+    bad = _lib.AttnDesc(4, 32, 8, 128, 16, 8, 1000, 1024, 0.088)       # table too narrow
+    assert lib.bi_paged_decode_attn(*args, ctypes.byref(bad), P(ok), 1 << 30, None) == -2
+    bad = _lib.AttnDesc(4, 24, 8, 128, 16, 64, 1000, 1024, 0.088)      # group of 3
+    assert lib.bi_paged_decode_attn(*args, ctypes.byref(bad), P(ok), 1 << 30, None) == -3
+    assert lib.bi_paged_decode_attn(None, *args[1:], ctypes.byref(d), P(ok), need, None) == -1
+
+
+def test_static_lint_no_float_atomics_or_cu_count_in_invariant_paths():
+    """Code-review rule of the Determinism article (section 8): no float
+    atomics, and no reduction order that depends on the number of compute
+    units.  Float atomics are banned everywhere; the CU count may be read
+    only by the fast twins' planners."""
+    csrc = os.path.join(ROOT, "invariant_bi_gemm_02_amd", "csrc")
+    for fn in os.listdir(csrc):
+        text = open(os.path.join(csrc, fn)).read()
+        assert not re.search(r"atomicAdd\s*\(\s*\(?\s*float", text), fn
+        assert "unsafeAtomicAdd" not in text, fn
+        for m in re.finditer(r"__hip_atomic_fetch_add\s*\(([^,]+),", text):
+            assert "ctr" in m.group(1), f"{fn}: atomic on {m.group(1)}"
+        if "MultiprocessorCount" in text or "multiProcessorCount" in text:
+            assert fn == "bi_api.hip", fn
