@@ -31,12 +31,10 @@
  *   - Errors are reported by the return code only; nothing is printed and
  *     nothing aborts.  On an error nothing is enqueued.
  *   - Workspace: operations that need one take (ws, ws_bytes), sized by the
- *     matching *_workspace_bytes query.  The first BI_WS_COUNTER_BYTES of a
- *     workspace hold integer arrival counters: they must be zero before the
- *     first call that uses the workspace (e.g. one hipMemset after
- *     allocating it), and every completed call leaves them zero again.  One
- *     workspace may be reused by any sequence of calls on one stream;
- *     concurrent calls must use distinct workspaces.
+ *     matching *_workspace_bytes query (0 means ws may be NULL).  It is
+ *     scratch: its contents need no initialisation and are undefined after
+ *     the call.  One workspace may be reused by any sequence of calls on one
+ *     stream; concurrent calls must use distinct workspaces.
  *   - No global mutable state: concurrent calls on different streams with
  *     distinct workspaces are safe.
  *   - Determinism contract (bi_* entry points, not the _fast twins): the
@@ -69,9 +67,6 @@ enum {
     BI_ERR_HIP = -5          /* the HIP launch itself failed                 */
 };
 
-/* Bytes at the start of every workspace that hold arrival counters. */
-#define BI_WS_COUNTER_BYTES 65536
-
 /* Library version, gfx target and every schedule constant, as one static
  * NUL-terminated string.  [Article] section 6: record the exact kernel
  * library and compile flags next to every result. */
@@ -98,7 +93,7 @@ const char *bi_status_string(int status);
  * only for rows < M.  Requirements: M, N, K >= 1; K % 32 == 0; N % 64 == 0;
  * M*K, K*N, M*N < 2^31; else BI_ERR_SHAPE / BI_ERR_UNSUPPORTED.
  * ws/ws_bytes: workspace of at least bi_gemm_workspace_bytes(M,N,K) bytes
- * (fp32 segment partials plus the counter region).
+ * (fp32 segment sums when they have to leave the compute unit; 0 otherwise).
  * ---------------------------------------------------------------------- */
 size_t bi_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int bi_gemm(const bi_bf16 *x, const bi_bf16 *W, bi_bf16 *y,

@@ -14,7 +14,6 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbi.so")
-WS_COUNTER_BYTES = 65536
 
 _STATUS = {0: "BI_OK", -1: "BI_ERR_NULL", -2: "BI_ERR_SHAPE", -3: "BI_ERR_UNSUPPORTED",
            -4: "BI_ERR_WORKSPACE", -5: "BI_ERR_HIP"}
@@ -84,20 +83,16 @@ def version() -> str:
 
 
 class Workspace:
-    """A zero-initialised device workspace that grows on demand.
-
-    The library needs the first 64 KiB (arrival counters) to be zero on entry
-    and leaves them zero; the rest is scratch.  One Workspace per stream.
-    """
+    """A device scratch buffer that grows on demand (one per stream)."""
 
     def __init__(self, device=None):
         self.device = torch.device(device or "cuda")
         self.buf = None
 
     def get(self, nbytes: int) -> torch.Tensor:
-        nbytes = max(int(nbytes), WS_COUNTER_BYTES)
+        nbytes = max(int(nbytes), 256)
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return self.buf
 
 

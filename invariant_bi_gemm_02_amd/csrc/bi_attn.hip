@@ -240,7 +240,7 @@ static int nc_stride_of(const bi_attn_desc* d, bool fast, int num_cus) {
 
 size_t attn_ws_bytes(const bi_attn_desc* d, bool fast, int num_cus) {
   const size_t nc = (size_t)nc_stride_of(d, fast, num_cus);
-  return WS_COUNTER_BYTES + (size_t)d->batch * d->num_q_heads * nc * APART * sizeof(float);
+  return (size_t)d->batch * d->num_q_heads * nc * APART * sizeof(float);
 }
 
 int launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* block_table,
@@ -250,7 +250,7 @@ int launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* block_tabl
   const int ncs = nc_stride_of(d, fast, num_cus);
   if (ws_bytes < attn_ws_bytes(d, fast, num_cus)) return BI_ERR_WORKSPACE;
   if (ncs > 65535 || d->num_kv_heads > 65535 || d->batch > 65535) return BI_ERR_UNSUPPORTED;
-  float* part = (float*)((char*)ws + WS_COUNTER_BYTES);
+  float* part = (float*)ws;
   const int fixed = fast ? 0 : ACHUNK;
   const int splits = fast ? ncs : 0;
   dim3 grid((unsigned)ncs, (unsigned)d->num_kv_heads, (unsigned)d->batch);

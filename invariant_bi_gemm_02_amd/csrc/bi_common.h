@@ -50,6 +50,16 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* lds_addr) {
 }
 
 __device__ __forceinline__ u32x4_t ldg128(const void* p) { return *(const u32x4_t*)p; }
+
+// Buffer resource over [base, base + bytes): raw (unswizzled) addressing with
+// a 32-bit byte offset; reads at offsets >= bytes return zero in hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4_t bufld128(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
 __device__ __forceinline__ void stg128(void* p, const u32x4_t& v) { *(u32x4_t*)p = v; }
 
 }  // namespace bi

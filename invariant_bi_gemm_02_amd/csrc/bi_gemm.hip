@@ -52,10 +52,9 @@ static constexpr int SPLIT_LDW = SPLIT_BN + 16;  // padded LDS row (elements)
 // MAXSUB = 1 for M <= 16 (fewer registers), 4 otherwise.
 template <int MAXSUB>
 __global__ __launch_bounds__(256) void gemm_split_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, uint16_t* __restrict__ y,
-    float* __restrict__ part, int* __restrict__ counters, int M, int N, int K, int KC, int S) {
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
+    float* __restrict__ part, int M, int N, int K, int KC) {
   __shared__ __attribute__((aligned(16))) uint16_t wl[2][SPLIT_SK * SPLIT_LDW];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -160,29 +159,149 @@ __global__ __launch_bounds__(256) void gemm_split_kernel(
     }
   }
 
-  // Arrival ticket: the last workgroup of this (mtile, ntile) folds.  The
-  // ticket decides only which workgroup folds, never the order of the adds.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  int* ctr = counters + (size_t)mtile * gridDim.x + ntile;
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (old == S - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
 
-  // Fold the S segment partials left to right: y32 = p0; y32 = y32 + p_s.
-  const int col = n0 + (tid & 63);
-  for (int r = tid >> 6; r < rows; r += 4) {
-    const int m = m0 + r;
-    const float* p = part + (size_t)m * N + col;
-    float y32 = p[0];
-    for (int s = 1; s < S; ++s) y32 = y32 + p[(size_t)s * M * N];
-    y[(size_t)m * N + col] = (uint16_t)f32_to_bf16_bits(y32);
+// ---------------------------------------------------------------------------
+// Skinny kernel (M <= 16, the decode regime: W streamed once, HBM bound)
+// ---------------------------------------------------------------------------
+// One workgroup of 512 lanes owns a 64-column tile of y (128-byte rows of W,
+// so every W line fetched is used whole) and either
+//   ALLK = false: one 512-row segment of K; its sum goes to the workspace and
+//                 gemm_fold_kernel adds the segments in order afterwards, or
+//   ALLK = true:  every segment of K in order, folded in registers, y written
+//                 directly (used when the 64-column tiles alone fill the chip).
+// The whole 64 KB W slab of a segment is requested at once (8 loads of 16 B
+// per lane) and the next segment's slab is in flight while the current one
+// is multiplied.  The slab sits in LDS with its 16-byte chunks XOR-swizzled
+// by row, so the transpose reads of four consecutive rows hit distinct banks.
+// Waves 0..3 each own one 16-column sub-tile; x fragments come straight from
+// memory (rows >= M read as zero through the buffer range check).
+static constexpr int SK_BN = 64;
+static constexpr int SK_ROWS = 512;  // = KC
+
+__device__ __forceinline__ int sk_phys(int row, int chunk) {  // element offset of a 16-B chunk
+  return row * SK_BN + ((chunk ^ (row & 7)) << 3);
+}
+
+template <bool ALLK>
+__global__ __launch_bounds__(512) void gemm_skinny_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, uint16_t* __restrict__ y,
+    float* __restrict__ part, int M, int N, int K, int S) {
+  __shared__ __attribute__((aligned(16))) uint16_t wl[SK_ROWS * SK_BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int arow = lane & 15;
+  const int tr_r = (lane & 15) >> 2;
+  const int tr_c = lane & 3;
+  const int n0 = blockIdx.x * SK_BN;
+  const int seg_begin = ALLK ? 0 : (int)blockIdx.y;
+  const int seg_end = ALLK ? S : (int)blockIdx.y + 1;
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)((size_t)K * N * 2));
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
+  const uint32_t row_bytes = (uint32_t)N * 2;
+
+  // W slab of one segment: chunk c = tid + 512 i is row c/8, 16-B chunk c%8.
+  u32x4_t wreg[8];
+  auto issue_w = [&](int seg, bool valid) {
+    uint32_t off = (uint32_t)(seg * SK_ROWS + (tid >> 3)) * row_bytes +
+                   (uint32_t)(n0 + (tid & 7) * 8) * 2;
+    if (!valid) off = 0x80000000u;  // past the end: zeros, no memory traffic
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      wreg[i] = bufld128(wr, off);
+      off = valid ? off + 64 * row_bytes : off;
+    }
+  };
+  u32x4_t xc[16];
+  auto issue_x = [&](int seg) {
+    const uint32_t off = (uint32_t)(arow * K + seg * SK_ROWS + g * 8) * 2;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) xc[j] = bufld128(xr, off + j * KB * 2);
+  };
+
+  f32x4_t tot = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  issue_w(seg_begin, true);
+  for (int seg = seg_begin; seg < seg_end; ++seg) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 512 * i;
+      *(u32x4_t*)&wl[sk_phys(c >> 3, c & 7)] = wreg[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (wave < 4) issue_x(seg);
+    issue_w(seg + 1, seg + 1 < seg_end);
+    if (wave < 4) {
+      const int nkb = min(SK_ROWS, K - seg * SK_ROWS) / KB;
+      const int chunk = 2 * wave + (tr_c >> 1);
+      const int sub = (tr_c & 1) * 4;
+      f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 16; ++kb) {
+        if (kb < nkb) {
+          const int r0 = kb * KB + 8 * g + tr_r;
+          const u32x2_t b0 = lds_read_tr16(&wl[sk_phys(r0, chunk) + sub]);
+          const u32x2_t b1 = lds_read_tr16(&wl[sk_phys(r0 + 4, chunk) + sub]);
+          a = mfma16x16x32(xc[kb], u32x4_t{b0.x, b0.y, b1.x, b1.y}, a);
+        }
+      }
+      const int col = n0 + 16 * wave + arow;
+      if (ALLK) {
+        if (seg == 0)
+          tot = a;
+        else
+          tot = tot + a;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = g * 4 + e;
+          if (m < M) part[((size_t)seg * M + m) * N + col] = a[e];
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   }
-  if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (ALLK && wave < 4) {
+    const int col = n0 + 16 * wave + arow;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = g * 4 + e;
+      if (m < M) y[(size_t)m * N + col] = (uint16_t)f32_to_bf16_bits(tot[e]);
+    }
+  }
+}
+
+// Ordered fold of segment sums: y = bf16(((p0 + p1) + p2) + ...), fp32.
+// One lane per (row, 4 columns); every segment's load is issued before the
+// adds.  grid = (ceil(N/256), M), block = 64.
+__global__ __launch_bounds__(64) void gemm_fold_kernel(const float* __restrict__ part,
+                                                       uint16_t* __restrict__ y, int M, int N,
+                                                       int S) {
+  const int c4 = blockIdx.x * 64 + threadIdx.x;
+  const int m = blockIdx.y;
+  if (c4 * 4 >= N) return;
+  const f32x4_t* p = (const f32x4_t*)(part + (size_t)m * N) + c4;
+  const size_t step = (size_t)M * N / 4;
+  f32x4_t acc = p[0];
+  for (int s0 = 1; s0 < S; s0 += 8) {
+    f32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) v[u] = p[(size_t)(s0 + u) * step];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) acc = acc + v[u];
+  }
+  uint32_t* out = (uint32_t*)(y + (size_t)m * N + c4 * 4);
+  out[0] = pack_bf16x2(acc[0], acc[1]);
+  out[1] = pack_bf16x2(acc[2], acc[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -343,54 +462,35 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
 // ---------------------------------------------------------------------------
 static constexpr int BI_KC = 512;  // invariant segment length
 static constexpr int SPLIT_MAX_M = 64;
-
-size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t S) {
-  return (size_t)S * (size_t)M * (size_t)N * sizeof(float);
-}
+static constexpr int SKINNY_MAX_M = 16;
+static constexpr int SKINNY_ALLK_TILES = 256;  // 64-column tiles that fill the chip alone
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool fast, int num_cus) {
-  if (M > SPLIT_MAX_M) return 0;  // the tile kernel needs no workspace
-  int64_t S;
-  if (!fast) {
-    S = ceil_div(K, BI_KC);
-  } else {
-    const int64_t KC = fast_split_kc(M, N, K, num_cus);
-    S = ceil_div(K, KC);
-  }
-  return WS_COUNTER_BYTES + gemm_split_ws_bytes(M, N, S);
+// Which kernels run for (M, N, K).  The bits never depend on it.
+enum class GemmPath { Tile, SkinnyAllK, SkinnySeg, Split };
+static GemmPath gemm_path(int64_t M, int64_t N) {
+  if (M > SPLIT_MAX_M) return GemmPath::Tile;
+  if (M <= SKINNY_MAX_M) return (N / SK_BN >= SKINNY_ALLK_TILES) ? GemmPath::SkinnyAllK
+                                                                  : GemmPath::SkinnySeg;
+  return GemmPath::Split;
 }
 
-// K slice of the fast twin: enough slices to give ~2 workgroups per CU.
-int64_t fast_split_kc(int64_t M, int64_t N, int64_t K, int num_cus) {
-  const int64_t tiles = (N / SPLIT_BN) * ceil_div(M, SPLIT_BM);
-  int64_t splits = ceil_div(2 * (int64_t)num_cus, tiles);
-  splits = std::max<int64_t>(1, std::min<int64_t>(splits, K / KB));
-  int64_t kc = ceil_div(ceil_div(K, splits), KB) * KB;
-  return kc;
+// The fast twin keeps the invariant kernels at M <= 64 (their schedule is
+// already the fastest layout for streaming W) and differs at large M.
+int64_t fast_split_kc(int64_t, int64_t, int64_t, int) { return BI_KC; }
+
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool, int) {
+  const GemmPath p = gemm_path(M, N);
+  if (p == GemmPath::Tile || p == GemmPath::SkinnyAllK) return 0;
+  return (size_t)ceil_div(K, BI_KC) * (size_t)M * (size_t)N * sizeof(float);
 }
 
 int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, int64_t N,
-                int64_t K, void* ws, size_t ws_bytes, hipStream_t stream, bool fast,
-                int num_cus) {
-  if (M <= SPLIT_MAX_M) {
-    const int64_t KC = fast ? fast_split_kc(M, N, K, num_cus) : BI_KC;
-    const int64_t S = ceil_div(K, KC);
-    const int64_t mt = ceil_div(M, SPLIT_BM), nt = N / SPLIT_BN;
-    if (mt * nt * (int64_t)sizeof(int) > WS_COUNTER_BYTES) return BI_ERR_UNSUPPORTED;
-    if (S > 65535) return BI_ERR_UNSUPPORTED;
-    if (ws_bytes < WS_COUNTER_BYTES + gemm_split_ws_bytes(M, N, S)) return BI_ERR_WORKSPACE;
-    int* counters = (int*)ws;
-    float* part = (float*)((char*)ws + WS_COUNTER_BYTES);
-    dim3 grid((unsigned)nt, (unsigned)S, (unsigned)mt);
-    if (M <= 16)
-      hipLaunchKernelGGL(gemm_split_kernel<1>, grid, dim3(256), 0, stream, x, W, y, part,
-                         counters, (int)M, (int)N, (int)K, (int)KC, (int)S);
-    else
-      hipLaunchKernelGGL(gemm_split_kernel<4>, grid, dim3(256), 0, stream, x, W, y, part,
-                         counters, (int)M, (int)N, (int)K, (int)KC, (int)S);
-  } else {
+                int64_t K, void* ws, size_t ws_bytes, hipStream_t stream, bool fast, int) {
+  const int64_t S = ceil_div(K, BI_KC);
+  const GemmPath p = gemm_path(M, N);
+  if (p == GemmPath::Tile) {
     dim3 grid((unsigned)ceil_div(N, TBN), (unsigned)ceil_div(M, TBM));
     if (fast)
       hipLaunchKernelGGL(gemm_tile_kernel<false>, grid, dim3(256), 0, stream, x, W, y, (int)M,
@@ -398,7 +498,27 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
     else
       hipLaunchKernelGGL(gemm_tile_kernel<true>, grid, dim3(256), 0, stream, x, W, y, (int)M,
                          (int)N, (int)K, BI_KC);
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
   }
+  if (p == GemmPath::SkinnyAllK) {
+    hipLaunchKernelGGL(gemm_skinny_kernel<true>, dim3((unsigned)(N / SK_BN), 1), dim3(512), 0,
+                       stream, x, W, y, (float*)nullptr, (int)M, (int)N, (int)K, (int)S);
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+  }
+  if (S > 65535) return BI_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < (size_t)S * (size_t)M * (size_t)N * sizeof(float)) return BI_ERR_WORKSPACE;
+  float* part = (float*)ws;
+  if (p == GemmPath::SkinnySeg) {
+    hipLaunchKernelGGL(gemm_skinny_kernel<false>, dim3((unsigned)(N / SK_BN), (unsigned)S),
+                       dim3(512), 0, stream, x, W, y, part, (int)M, (int)N, (int)K, (int)S);
+  } else {
+    dim3 grid((unsigned)(N / SPLIT_BN), (unsigned)S, (unsigned)ceil_div(M, SPLIT_BM));
+    hipLaunchKernelGGL(gemm_split_kernel<4>, grid, dim3(256), 0, stream, x, W, part, (int)M,
+                       (int)N, (int)K, BI_KC);
+  }
+  if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
+  hipLaunchKernelGGL(gemm_fold_kernel, dim3((unsigned)ceil_div(N, 256), (unsigned)M), dim3(64),
+                     0, stream, part, y, (int)M, (int)N, (int)S);
   return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 

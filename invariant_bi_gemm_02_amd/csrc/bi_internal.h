@@ -10,8 +10,6 @@
 
 namespace bi {
 
-static constexpr size_t WS_COUNTER_BYTES = BI_WS_COUNTER_BYTES;
-
 // GEMM (bi_gemm.hip)
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool fast, int num_cus);
 int64_t fast_split_kc(int64_t M, int64_t N, int64_t K, int num_cus);
