@@ -62,4 +62,18 @@ __device__ __forceinline__ u32x4_t bufld128(__amdgpu_buffer_rsrc_t r, uint32_t b
 }
 __device__ __forceinline__ void stg128(void* p, const u32x4_t& v) { *(u32x4_t*)p = v; }
 
+// Direct-to-LDS load: every lane fetches 16 bytes at byte offset `off` of the
+// buffer; lane i's bytes land at lds_base + 16 i.  Reads past the end of the
+// buffer deposit zeros.  Completion is counted by vmcnt, not by any register.
+__device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (BI_LDS void*)lds_base, 16, off, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained), N < 16.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 }  // namespace bi

@@ -458,6 +458,200 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Tile kernel v3 (large M, matrix-core bound)
+// ---------------------------------------------------------------------------
+// 256 x 128 output tile per workgroup of 8 waves (4 x 2), each wave 64 x 64
+// (4 x 4 matrix-core tiles), two waves per SIMD.  K advances in stages of 64
+// (two K-blocks): the next stage's x slab (256 x 64) and W slab (64 x 128)
+// are fetched into registers while the current stage is multiplied out of
+// LDS, then written to the other of two LDS stage buffers.  LDS rows are
+// XOR-swizzled in 16-byte chunks so that the A-operand reads (8 rows at a
+// time) and the transpose reads of W (4 rows at a time) hit distinct banks.
+// FOLD: segments of KC from +0 folded in order in registers (batch-invariant
+// schedule); without FOLD one accumulation chain runs over all of K.
+// Workgroups are mapped to tiles so that each XCD (workgroups are dispatched
+// to the 8 XCDs round robin) works on a contiguous band of tiles, m fastest:
+// workgroups sharing an L2 share W column panels and x row panels.
+static constexpr int T2_BM = 256, T2_BN = 128, T2_BK = 64;
+static constexpr int T2_XS = T2_BM * T2_BK;          // x slab elements (32 KB)
+static constexpr int T2_WS = T2_BK * T2_BN;          // W slab elements (16 KB)
+static constexpr int T2_STAGE = T2_XS + T2_WS;       // 48 KB per stage buffer
+
+// element offset of logical 16-B chunk `c` of row `r` in the x slab (8 chunks per row)
+__device__ __forceinline__ int t2_xphys(int r, int c) { return r * T2_BK + ((c ^ (r & 7)) << 3); }
+// element offset of logical 16-B chunk `c` of k-row `r` in the W slab (16 chunks per row)
+__device__ __forceinline__ int t2_wphys(int r, int c) { return T2_XS + r * T2_BN + ((c ^ ((r & 3) << 1)) << 3); }
+
+template <bool FOLD>
+__global__ __launch_bounds__(512, 1) void gemm_tile2_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, uint16_t* __restrict__ y,
+    int M, int N, int K, int KC, int tm, int tn, int remap) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][T2_STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const int tr_r = l16 >> 2, tr_c = lane & 3;
+
+  int t = blockIdx.x;
+  if (remap) t = (t & 7) * ((tm * tn) >> 3) + (t >> 3);
+  const int m0 = (t % tm) * T2_BM;
+  const int n0 = (t / tm) * T2_BN;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)((size_t)K * N * 2));
+
+  // Loads of one stage: x chunks c = tid + 512 i (row c/8, chunk c%8), W
+  // chunks c = tid + 512 i (k-row c/16, chunk c%16).  Rows >= M and k >= K
+  // read as zero through the buffer range check.
+  const uint32_t xoff0 = (uint32_t)((m0 + (tid >> 3)) * K + (tid & 7) * 8) * 2;
+  const uint32_t xrow64 = (uint32_t)K * 2 * 64;   // 64 rows of x, in bytes
+  const uint32_t woff0 = (uint32_t)((tid >> 4) * N + n0 + (tid & 15) * 8) * 2;
+  const uint32_t wrow32 = (uint32_t)N * 2 * 32;   // 32 k-rows of W, in bytes
+  // Two register sets: stage st+1 waits in one while stage st+2 is fetched
+  // into the other, so global loads get two stages of multiplies to land.
+  u32x4_t xs[2][4], ws[2][2];
+  auto load_stage = [&](int k0, int set) {
+    const bool valid = k0 < K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      xs[set][i] = bufld128(xr, valid ? xoff0 + i * xrow64 + (uint32_t)k0 * 2 : 0x80000000u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      ws[set][i] = bufld128(wr, valid ? woff0 + i * wrow32 + (uint32_t)k0 * N * 2 : 0x80000000u);
+  };
+  auto store_stage = [&](uint16_t* buf, int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 512 * i;
+      *(u32x4_t*)(buf + t2_xphys(c >> 3, c & 7)) = xs[set][i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 512 * i;
+      *(u32x4_t*)(buf + t2_wphys(c >> 4, c & 15)) = ws[set][i];
+    }
+  };
+
+  f32x4_t acc[4][4];
+  f32x4_t tot[FOLD ? 4 : 1][FOLD ? 4 : 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < (FOLD ? 4 : 1); ++i)
+#pragma unroll
+    for (int j = 0; j < (FOLD ? 4 : 1); ++j) tot[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int wrow0 = m0 + wm * 64;
+  const int nsub = max(0, min(4, (M - wrow0 + 15) >> 4));
+  const int blocks_per_seg = KC / KB;
+  int kblk = 0;  // K-blocks done in the current segment
+  int seg = 0;
+
+  // LDS element offsets of this lane's operand reads (K-block j adds 4 chunks
+  // (x) or 32 rows (W), both applied below).
+  int aoff[4][2], boff[4][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) aoff[s][j] = t2_xphys(wm * 64 + s * 16 + l16, j * 4 + g);
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int col = wn * 64 + tt * 16 + 4 * tr_c;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      boff[tt][h] = t2_wphys(8 * g + 4 * h + tr_r, col >> 3) + (col & 7);
+  }
+
+  auto compute = [&](const uint16_t* buf, int k0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (k0 + j * KB < K) {
+        u32x4_t bf[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          // W k-rows of K-block j sit 32 rows further down; the swizzle uses
+          // row % 4, which is unchanged by a 32-row step
+          const u32x2_t b0 = lds_read_tr16(buf + boff[tt][0] + j * KB * T2_BN);
+          const u32x2_t b1 = lds_read_tr16(buf + boff[tt][1] + j * KB * T2_BN);
+          bf[tt] = u32x4_t{b0.x, b0.y, b1.x, b1.y};
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (s < nsub) {
+            const u32x4_t af = *(const u32x4_t*)(buf + aoff[s][j]);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) acc[s][tt] = mfma16x16x32(af, bf[tt], acc[s][tt]);
+          }
+        }
+        if (FOLD) {
+          if (++kblk == blocks_per_seg || k0 + (j + 1) * KB >= K) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+              for (int tt = 0; tt < 4; ++tt) {
+                if (seg == 0)
+                  tot[s][tt] = acc[s][tt];
+                else
+                  tot[s][tt] = tot[s][tt] + acc[s][tt];
+                acc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+              }
+            ++seg;
+            kblk = 0;
+          }
+        }
+      }
+    }
+  };
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
+  // Pipeline: LDS buffer st%2 holds stage st, register set (st+1)%2 holds
+  // stage st+1, and stage st+2 is fetched into register set st%2.
+  const int nstage = (K + T2_BK - 1) / T2_BK;
+  load_stage(0, 0);
+  load_stage(T2_BK, 1);
+  store_stage(lds[0], 0);
+  lds_barrier();
+  for (int st = 0; st < nstage; st += 2) {
+    load_stage((st + 2) * T2_BK, 0);
+    compute(lds[0], st * T2_BK);
+    if (st + 1 >= nstage) break;
+    store_stage(lds[1], 1);
+    lds_barrier();
+    load_stage((st + 3) * T2_BK, 1);
+    compute(lds[1], (st + 1) * T2_BK);
+    if (st + 2 >= nstage) break;
+    store_stage(lds[0], 0);
+    lds_barrier();
+  }
+
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s < nsub) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int col = n0 + wn * 64 + tt * 16 + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = wrow0 + s * 16 + g * 4 + e;
+          const float v = FOLD ? tot[s][tt][e] : acc[s][tt][e];
+          if (m < M && col < N) y[(size_t)m * N + col] = (uint16_t)f32_to_bf16_bits(v);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 static constexpr int BI_KC = 512;  // invariant segment length
@@ -491,13 +685,15 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
   const int64_t S = ceil_div(K, BI_KC);
   const GemmPath p = gemm_path(M, N);
   if (p == GemmPath::Tile) {
-    dim3 grid((unsigned)ceil_div(N, TBN), (unsigned)ceil_div(M, TBM));
+    const int64_t tm = ceil_div(M, T2_BM), tn = ceil_div(N, T2_BN);
+    const int remap = ((tm * tn) % 8 == 0) ? 1 : 0;
+    dim3 grid((unsigned)(tm * tn));
     if (fast)
-      hipLaunchKernelGGL(gemm_tile_kernel<false>, grid, dim3(256), 0, stream, x, W, y, (int)M,
-                         (int)N, (int)K, (int)K);
+      hipLaunchKernelGGL(gemm_tile2_kernel<false>, grid, dim3(512), 0, stream, x, W, y, (int)M,
+                         (int)N, (int)K, (int)K, (int)tm, (int)tn, remap);
     else
-      hipLaunchKernelGGL(gemm_tile_kernel<true>, grid, dim3(256), 0, stream, x, W, y, (int)M,
-                         (int)N, (int)K, BI_KC);
+      hipLaunchKernelGGL(gemm_tile2_kernel<true>, grid, dim3(512), 0, stream, x, W, y, (int)M,
+                         (int)N, (int)K, BI_KC, (int)tm, (int)tn, remap);
     return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
   }
   if (p == GemmPath::SkinnyAllK) {
