@@ -581,14 +581,16 @@ __global__ __launch_bounds__(512, 1) void gemm_tile2_kernel(
           const u32x2_t b1 = lds_read_tr16(buf + boff[tt][1] + j * KB * T2_BN);
           bf[tt] = u32x4_t{b0.x, b0.y, b1.x, b1.y};
         }
+        // every 16-row sub-tile is multiplied, padding rows included (they
+        // hold zeros and are never stored): no per-sub-tile branch, so the
+        // A-operand reads can all be issued ahead of the multiplies
+        u32x4_t af[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (s < nsub) {
-            const u32x4_t af = *(const u32x4_t*)(buf + aoff[s][j]);
+        for (int s = 0; s < 4; ++s) af[s] = *(const u32x4_t*)(buf + aoff[s][j]);
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) acc[s][tt] = mfma16x16x32(af, bf[tt], acc[s][tt]);
-          }
-        }
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) acc[s][tt] = mfma16x16x32(af[s], bf[tt], acc[s][tt]);
         if (FOLD) {
           if (++kblk == blocks_per_seg || k0 + (j + 1) * KB >= K) {
 #pragma unroll
