@@ -472,20 +472,31 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(
 // Workgroups are mapped to tiles so that each XCD (workgroups are dispatched
 // to the 8 XCDs round robin) works on a contiguous band of tiles, m fastest:
 // workgroups sharing an L2 share W column panels and x row panels.
-static constexpr int T2_BM = 256, T2_BN = 128, T2_BK = 64;
-static constexpr int T2_XS = T2_BM * T2_BK;          // x slab elements (32 KB)
+static constexpr int T2_BN = 128, T2_BK = 64;
 static constexpr int T2_WS = T2_BK * T2_BN;          // W slab elements (16 KB)
-static constexpr int T2_STAGE = T2_XS + T2_WS;       // 48 KB per stage buffer
 
 // element offset of logical 16-B chunk `c` of row `r` in the x slab (8 chunks per row)
 __device__ __forceinline__ int t2_xphys(int r, int c) { return r * T2_BK + ((c ^ (r & 7)) << 3); }
-// element offset of logical 16-B chunk `c` of k-row `r` in the W slab (16 chunks per row)
-__device__ __forceinline__ int t2_wphys(int r, int c) { return T2_XS + r * T2_BN + ((c ^ ((r & 3) << 1)) << 3); }
+// element offset of logical 16-B chunk `c` of k-row `r` in the W slab (16 chunks
+// per row), which follows an x slab of `xs` elements
+__device__ __forceinline__ int t2_wphys(int xs, int r, int c) {
+  return xs + r * T2_BN + ((c ^ ((r & 3) << 1)) << 3);
+}
 
-template <bool FOLD>
-__global__ __launch_bounds__(512, 1) void gemm_tile2_kernel(
+// BM rows per workgroup, 2*BM lanes (BM/64 x 2 waves of 64 x 64).  256 is the
+// size in use: with the fold's second set of accumulators, 128 spills.
+// SLICE: the workgroup covers only K slice blockIdx.y ([y*KC, y*KC + KC)),
+// accumulated in one chain from +0, and writes the fp32 slice sum to
+// part[y][M][N] for gemm_fold_kernel (used when the tiles alone are too few
+// to fill the chip; with KC = 512 the slice is exactly one segment).
+template <bool FOLD, int BM, bool SLICE = false>
+__global__ __launch_bounds__(BM * 2, 2) void gemm_tile2_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, uint16_t* __restrict__ y,
-    int M, int N, int K, int KC, int tm, int tn, int remap) {
+    int M, int N, int K, int KC, int tm, int tn, int remap, float* __restrict__ part = nullptr) {
+  constexpr int NT = BM * 2;                  // lanes per workgroup
+  constexpr int T2_BM = BM;
+  constexpr int T2_XS = BM * T2_BK;           // x slab elements
+  constexpr int T2_STAGE = T2_XS + T2_WS;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][T2_STAGE];
 
   const int tid = threadIdx.x;
@@ -503,36 +514,39 @@ __global__ __launch_bounds__(512, 1) void gemm_tile2_kernel(
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)((size_t)K * N * 2));
+  // K range of this workgroup: all of K, or one slice
+  const int kbeg = SLICE ? (int)blockIdx.y * KC : 0;
+  const int kend = SLICE ? min(K, kbeg + KC) : K;
 
-  // Loads of one stage: x chunks c = tid + 512 i (row c/8, chunk c%8), W
-  // chunks c = tid + 512 i (k-row c/16, chunk c%16).  Rows >= M and k >= K
+  // Loads of one stage: x chunks c = tid + NT i (row c/8, chunk c%8), W
+  // chunks c = tid + NT i (k-row c/16, chunk c%16).  Rows >= M and k >= K
   // read as zero through the buffer range check.
+  constexpr int XL = T2_XS / 8 / NT;          // 16-B x chunks per lane per stage (4)
+  constexpr int WL = T2_WS / 8 / NT;          // 16-B W chunks per lane per stage (2 or 4)
   const uint32_t xoff0 = (uint32_t)((m0 + (tid >> 3)) * K + (tid & 7) * 8) * 2;
-  const uint32_t xrow64 = (uint32_t)K * 2 * 64;   // 64 rows of x, in bytes
+  const uint32_t xrowstep = (uint32_t)K * 2 * (NT / 8);    // NT/8 rows of x, in bytes
   const uint32_t woff0 = (uint32_t)((tid >> 4) * N + n0 + (tid & 15) * 8) * 2;
-  const uint32_t wrow32 = (uint32_t)N * 2 * 32;   // 32 k-rows of W, in bytes
-  // Two register sets: stage st+1 waits in one while stage st+2 is fetched
-  // into the other, so global loads get two stages of multiplies to land.
-  u32x4_t xs[2][4], ws[2][2];
-  auto load_stage = [&](int k0, int set) {
-    const bool valid = k0 < K;
+  const uint32_t wrowstep = (uint32_t)N * 2 * (NT / 16);   // NT/16 k-rows of W, in bytes
+  u32x4_t xs[XL], ws[WL];
+  auto load_stage = [&](int k0) {
+    const bool valid = k0 < kend;   // past the end: zeros, no memory traffic
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      xs[set][i] = bufld128(xr, valid ? xoff0 + i * xrow64 + (uint32_t)k0 * 2 : 0x80000000u);
+    for (int i = 0; i < XL; ++i)
+      xs[i] = bufld128(xr, valid ? xoff0 + i * xrowstep + (uint32_t)k0 * 2 : 0x80000000u);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      ws[set][i] = bufld128(wr, valid ? woff0 + i * wrow32 + (uint32_t)k0 * N * 2 : 0x80000000u);
+    for (int i = 0; i < WL; ++i)
+      ws[i] = bufld128(wr, valid ? woff0 + i * wrowstep + (uint32_t)k0 * N * 2 : 0x80000000u);
   };
-  auto store_stage = [&](uint16_t* buf, int set) {
+  auto store_stage = [&](uint16_t* buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 512 * i;
-      *(u32x4_t*)(buf + t2_xphys(c >> 3, c & 7)) = xs[set][i];
+    for (int i = 0; i < XL; ++i) {
+      const int c = tid + NT * i;
+      *(u32x4_t*)(buf + t2_xphys(c >> 3, c & 7)) = xs[i];
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 512 * i;
-      *(u32x4_t*)(buf + t2_wphys(c >> 4, c & 15)) = ws[set][i];
+    for (int i = 0; i < WL; ++i) {
+      const int c = tid + NT * i;
+      *(u32x4_t*)(buf + t2_wphys(T2_XS, c >> 4, c & 15)) = ws[i];
     }
   };
 
@@ -553,61 +567,69 @@ __global__ __launch_bounds__(512, 1) void gemm_tile2_kernel(
   int kblk = 0;  // K-blocks done in the current segment
   int seg = 0;
 
-  // LDS element offsets of this lane's operand reads (K-block j adds 4 chunks
-  // (x) or 32 rows (W), both applied below).
-  int aoff[4][2], boff[4][2];
+  // LDS element offsets of this lane's operand reads for K-block 0 of a
+  // stage; sub-tile s adds 16 rows (the x swizzle uses row % 8, unchanged),
+  // K-block 1 adds 4 chunks (x) or 32 rows (W, swizzle uses row % 4).
+  int aoff[2], boff[4][2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) aoff[s][j] = t2_xphys(wm * 64 + s * 16 + l16, j * 4 + g);
+  for (int j = 0; j < 2; ++j) aoff[j] = t2_xphys(wm * 64 + l16, j * 4 + g);
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     const int col = wn * 64 + tt * 16 + 4 * tr_c;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      boff[tt][h] = t2_wphys(8 * g + 4 * h + tr_r, col >> 3) + (col & 7);
+      boff[tt][h] = t2_wphys(T2_XS, 8 * g + 4 * h + tr_r, col >> 3) + (col & 7);
   }
 
-  auto compute = [&](const uint16_t* buf, int k0) {
+  // operand fragments of one K-block: A for the 4 sub-tiles, B for the 4 columns
+  u32x4_t af[2][4], bf[2][4];
+  auto read_frags = [&](const uint16_t* buf, int j, int set) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (k0 + j * KB < K) {
-        u32x4_t bf[4];
+    for (int tt = 0; tt < 4; ++tt) {
+      const u32x2_t b0 = lds_read_tr16(buf + boff[tt][0] + j * KB * T2_BN);
+      const u32x2_t b1 = lds_read_tr16(buf + boff[tt][1] + j * KB * T2_BN);
+      bf[set][tt] = u32x4_t{b0.x, b0.y, b1.x, b1.y};
+    }
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          // W k-rows of K-block j sit 32 rows further down; the swizzle uses
-          // row % 4, which is unchanged by a 32-row step
-          const u32x2_t b0 = lds_read_tr16(buf + boff[tt][0] + j * KB * T2_BN);
-          const u32x2_t b1 = lds_read_tr16(buf + boff[tt][1] + j * KB * T2_BN);
-          bf[tt] = u32x4_t{b0.x, b0.y, b1.x, b1.y};
-        }
-        // every 16-row sub-tile is multiplied, padding rows included (they
-        // hold zeros and are never stored): no per-sub-tile branch, so the
-        // A-operand reads can all be issued ahead of the multiplies
-        u32x4_t af[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) af[s] = *(const u32x4_t*)(buf + aoff[s][j]);
+    for (int s = 0; s < 4; ++s)
+      af[set][s] = *(const u32x4_t*)(buf + aoff[j] + s * 16 * T2_BK);
+  };
+  auto fold_if_segment_end = [&](int kdone) {
+    if (FOLD) {
+      if (++kblk == blocks_per_seg || kdone >= kend) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) acc[s][tt] = mfma16x16x32(af[s], bf[tt], acc[s][tt]);
-        if (FOLD) {
-          if (++kblk == blocks_per_seg || k0 + (j + 1) * KB >= K) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-              for (int tt = 0; tt < 4; ++tt) {
-                if (seg == 0)
-                  tot[s][tt] = acc[s][tt];
-                else
-                  tot[s][tt] = tot[s][tt] + acc[s][tt];
-                acc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-              }
-            ++seg;
-            kblk = 0;
+          for (int tt = 0; tt < 4; ++tt) {
+            if (seg == 0)
+              tot[s][tt] = acc[s][tt];
+            else
+              tot[s][tt] = tot[s][tt] + acc[s][tt];
+            acc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           }
-        }
+        ++seg;
+        kblk = 0;
       }
+    }
+  };
+  // Multiply one stage: the fragments of K-block 1 are read while the
+  // multiplies of K-block 0 run.  Every 16-row sub-tile is multiplied,
+  // padding rows included (they hold zeros and are never stored).
+  auto compute = [&](const uint16_t* buf, int k0) {
+    read_frags(buf, 0, 0);
+    const bool two = k0 + KB < kend;
+    if (two) read_frags(buf, 1, 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[s][tt] = mfma16x16x32(af[0][s], bf[0][tt], acc[s][tt]);
+    fold_if_segment_end(k0 + KB);
+    if (two) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[s][tt] = mfma16x16x32(af[1][s], bf[1][tt], acc[s][tt]);
+      fold_if_segment_end(k0 + 2 * KB);
     }
   };
   auto lds_barrier = [&]() {
@@ -616,23 +638,14 @@ __global__ __launch_bounds__(512, 1) void gemm_tile2_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
-  // Pipeline: LDS buffer st%2 holds stage st, register set (st+1)%2 holds
-  // stage st+1, and stage st+2 is fetched into register set st%2.
-  const int nstage = (K + T2_BK - 1) / T2_BK;
-  load_stage(0, 0);
-  load_stage(T2_BK, 1);
-  store_stage(lds[0], 0);
+  const int nstage = (kend - kbeg + T2_BK - 1) / T2_BK;
+  load_stage(kbeg);
+  store_stage(lds[0]);
   lds_barrier();
-  for (int st = 0; st < nstage; st += 2) {
-    load_stage((st + 2) * T2_BK, 0);
-    compute(lds[0], st * T2_BK);
-    if (st + 1 >= nstage) break;
-    store_stage(lds[1], 1);
-    lds_barrier();
-    load_stage((st + 3) * T2_BK, 1);
-    compute(lds[1], (st + 1) * T2_BK);
-    if (st + 2 >= nstage) break;
-    store_stage(lds[0], 0);
+  for (int st = 0; st < nstage; ++st) {
+    load_stage(kbeg + (st + 1) * T2_BK);
+    compute(lds[st & 1], kbeg + st * T2_BK);
+    if (st + 1 < nstage) store_stage(lds[(st + 1) & 1]);
     lds_barrier();
   }
 
@@ -646,7 +659,12 @@ __global__ __launch_bounds__(512, 1) void gemm_tile2_kernel(
         for (int e = 0; e < 4; ++e) {
           const int m = wrow0 + s * 16 + g * 4 + e;
           const float v = FOLD ? tot[s][tt][e] : acc[s][tt][e];
-          if (m < M && col < N) y[(size_t)m * N + col] = (uint16_t)f32_to_bf16_bits(v);
+          if (m < M && col < N) {
+            if (SLICE)
+              part[((size_t)blockIdx.y * M + m) * N + col] = v;
+            else
+              y[(size_t)m * N + col] = (uint16_t)f32_to_bf16_bits(v);
+          }
         }
       }
     }
@@ -657,6 +675,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tile2_kernel(
 // Host side
 // ---------------------------------------------------------------------------
 static constexpr int BI_KC = 512;  // invariant segment length
+static constexpr int TILE_BM = 256;  // rows per tile-kernel workgroup (8 waves)
 static constexpr int SPLIT_MAX_M = 64;
 static constexpr int SKINNY_MAX_M = 16;
 static constexpr int SKINNY_ALLK_TILES = 256;  // 64-column tiles that fill the chip alone
@@ -664,38 +683,70 @@ static constexpr int SKINNY_ALLK_TILES = 256;  // 64-column tiles that fill the 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Which kernels run for (M, N, K).  The bits never depend on it.
-enum class GemmPath { Tile, SkinnyAllK, SkinnySeg, Split };
+static constexpr int TILE_MIN_TILES = 192;  // fewer tiles than this: split K into slices
+
+enum class GemmPath { Tile, TileSlice, SkinnyAllK, SkinnySeg, Split };
 static GemmPath gemm_path(int64_t M, int64_t N) {
-  if (M > SPLIT_MAX_M) return GemmPath::Tile;
+  if (M > SPLIT_MAX_M)
+    return ceil_div(M, TILE_BM) * ceil_div(N, T2_BN) >= TILE_MIN_TILES ? GemmPath::Tile
+                                                                         : GemmPath::TileSlice;
   if (M <= SKINNY_MAX_M) return (N / SK_BN >= SKINNY_ALLK_TILES) ? GemmPath::SkinnyAllK
                                                                   : GemmPath::SkinnySeg;
   return GemmPath::Split;
 }
 
-// The fast twin keeps the invariant kernels at M <= 64 (their schedule is
-// already the fastest layout for streaming W) and differs at large M.
-int64_t fast_split_kc(int64_t, int64_t, int64_t, int) { return BI_KC; }
+// K slice of the tile kernel: the invariant schedule always uses 512 (one
+// segment per slice); the fast twin uses as few slices as fill the chip.
+// At M <= 64 the fast twin keeps the invariant kernels (their schedule is
+// already the fastest layout for streaming W).
+int64_t fast_split_kc(int64_t M, int64_t N, int64_t K, int num_cus) {
+  const int64_t tiles = ceil_div(M, TILE_BM) * ceil_div(N, T2_BN);
+  const int64_t slices = std::max<int64_t>(1, ceil_div(std::max(num_cus, 1), tiles));
+  return ceil_div(ceil_div(K, slices), T2_BK) * T2_BK;
+}
+static int64_t slice_kc(int64_t M, int64_t N, int64_t K, bool fast, int num_cus) {
+  return fast ? fast_split_kc(M, N, K, num_cus) : BI_KC;
+}
 
-size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool, int) {
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool fast, int num_cus) {
   const GemmPath p = gemm_path(M, N);
   if (p == GemmPath::Tile || p == GemmPath::SkinnyAllK) return 0;
-  return (size_t)ceil_div(K, BI_KC) * (size_t)M * (size_t)N * sizeof(float);
+  const int64_t kc = p == GemmPath::TileSlice ? slice_kc(M, N, K, fast, num_cus) : BI_KC;
+  return (size_t)ceil_div(K, kc) * (size_t)M * (size_t)N * sizeof(float);
 }
 
 int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, int64_t N,
-                int64_t K, void* ws, size_t ws_bytes, hipStream_t stream, bool fast, int) {
+                int64_t K, void* ws, size_t ws_bytes, hipStream_t stream, bool fast, int num_cus) {
   const int64_t S = ceil_div(K, BI_KC);
   const GemmPath p = gemm_path(M, N);
   if (p == GemmPath::Tile) {
-    const int64_t tm = ceil_div(M, T2_BM), tn = ceil_div(N, T2_BN);
+    constexpr int BM = TILE_BM;
+    const int64_t tm = ceil_div(M, BM), tn = ceil_div(N, T2_BN);
     const int remap = ((tm * tn) % 8 == 0) ? 1 : 0;
     dim3 grid((unsigned)(tm * tn));
     if (fast)
-      hipLaunchKernelGGL(gemm_tile2_kernel<false>, grid, dim3(512), 0, stream, x, W, y, (int)M,
-                         (int)N, (int)K, (int)K, (int)tm, (int)tn, remap);
+      hipLaunchKernelGGL((gemm_tile2_kernel<false, BM>), grid, dim3(2 * BM), 0, stream, x, W, y,
+                         (int)M, (int)N, (int)K, (int)K, (int)tm, (int)tn, remap);
     else
-      hipLaunchKernelGGL(gemm_tile2_kernel<true>, grid, dim3(512), 0, stream, x, W, y, (int)M,
-                         (int)N, (int)K, BI_KC, (int)tm, (int)tn, remap);
+      hipLaunchKernelGGL((gemm_tile2_kernel<true, BM>), grid, dim3(2 * BM), 0, stream, x, W, y,
+                         (int)M, (int)N, (int)K, BI_KC, (int)tm, (int)tn, remap);
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+  }
+  if (p == GemmPath::TileSlice) {
+    constexpr int BM = TILE_BM;
+    const int64_t kc = slice_kc(M, N, K, fast, num_cus);
+    const int64_t ns = ceil_div(K, kc);
+    const int64_t tm = ceil_div(M, BM), tn = ceil_div(N, T2_BN);
+    if (ns > 65535) return BI_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < (size_t)ns * (size_t)M * (size_t)N * sizeof(float)) return BI_ERR_WORKSPACE;
+    float* part = (float*)ws;
+    const int remap = ((tm * tn) % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((gemm_tile2_kernel<false, BM, true>), dim3((unsigned)(tm * tn), (unsigned)ns),
+                       dim3(2 * BM), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)kc, (int)tm,
+                       (int)tn, remap, part);
+    if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
+    hipLaunchKernelGGL(gemm_fold_kernel, dim3((unsigned)ceil_div(N, 256), (unsigned)M), dim3(64),
+                       0, stream, part, y, (int)M, (int)N, (int)ns);
     return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
   }
   if (p == GemmPath::SkinnyAllK) {
