@@ -151,9 +151,9 @@ int bi_rmsnorm_fast(const bi_bf16 *x, const bi_bf16 *g, bi_bf16 *y,
  *              <= max_ctx_len and every referenced page < num_pages (device
  *              data is not range-checked).
  * out:         [batch, num_q_heads, head_dim] bf16.
- * Supported: head_dim == 128, page_size == 16, num_q_heads % num_kv_heads
- * == 0 with num_q_heads / num_kv_heads <= 8, batch >= 1, 1 <= max_ctx_len
- * <= max_blocks_per_seq * page_size.  max_ctx_len only sizes the grid and
+ * Supported: head_dim == 128, page_size == 16, num_q_heads / num_kv_heads
+ * in {1, 2, 4, 8}, batch >= 1, 1 <= max_ctx_len <= max_blocks_per_seq *
+ * page_size and max_ctx_len <= 262144.  max_ctx_len only sizes the grid and
  * the workspace; it never changes the bits.
  * ---------------------------------------------------------------------- */
 typedef struct {

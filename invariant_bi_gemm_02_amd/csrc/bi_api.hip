@@ -58,6 +58,7 @@ int check_attn(const void* q, const void* kv, const void* bt, const void* cl, co
   if ((int64_t)d->max_ctx_len > (int64_t)d->max_blocks_per_seq * d->page_size) return BI_ERR_SHAPE;
   if ((int64_t)d->batch * d->max_blocks_per_seq >= kMaxElems) return BI_ERR_SHAPE;
   if (d->head_dim != 128 || d->page_size != 16) return BI_ERR_UNSUPPORTED;
+  if (d->max_ctx_len > 262144) return BI_ERR_UNSUPPORTED;  // 1024 chunks of 256
   if (d->num_q_heads % d->num_kv_heads != 0) return BI_ERR_UNSUPPORTED;
   const int G = d->num_q_heads / d->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return BI_ERR_UNSUPPORTED;

@@ -34,6 +34,7 @@ static constexpr int ATILE = 64;      // tokens per tile
 static constexpr int ACHUNK = 256;    // tokens per chunk (batch-invariant entry point)
 static constexpr int APART = AD + 4;  // floats per partial: m, l, 2 pad, acc[128]
 static constexpr int AKLD = AD + 8;   // padded K row in LDS (elements)
+static constexpr int ACH = 256;       // longest chunk the fast twin may pick (combine bound)
 
 // Chunk length for request length L: fixed, or (fast twin) from the split count.
 __device__ __forceinline__ int chunk_len(int L, int fixed_chunk, int splits) {
@@ -168,7 +169,23 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
         float a0 = acc0[j] * alpha;
         float a1 = acc1[j] * alpha;
         const uint32_t* vcol = (const uint32_t*)vs + lane;  // dims 2 lane, 2 lane + 1
-        for (int i = 0; i < nt; ++i) {
+        int i = 0;
+        // eight tokens at a time: all LDS reads first, then the in-order chain
+        for (; i + 8 <= nt; i += 8) {
+          const f32x4_t pa = *(const f32x4_t*)&ps[hh][i];
+          const f32x4_t pb = *(const f32x4_t*)&ps[hh][i + 4];
+          uint32_t v2[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v2[u] = vcol[(i + u) * (AD / 2)];
+          const float pv[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            lj = lj + pv[u];
+            a0 = __fmaf_rn(pv[u], bf16_lo(v2[u]), a0);
+            a1 = __fmaf_rn(pv[u], bf16_hi(v2[u]), a1);
+          }
+        }
+        for (; i < nt; ++i) {
           const float p = ps[hh][i];
           const uint32_t v2 = vcol[i * (AD / 2)];
           lj = lj + p;
@@ -200,9 +217,17 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
 }
 
 // grid = (num_q_heads, batch), block = 128 (one lane per dim).
+// The chunk maxima and weights are computed by all lanes in parallel (the
+// maximum does not depend on order); the two sums then run in chunk order,
+// with the partials of 16 chunks fetched before each stretch of the chain.
+static constexpr int ACOMB_MAXC = 1024;  // chunks per request the combine handles
+
 __global__ __launch_bounds__(128) void attn_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ ctx_lens,
     uint16_t* __restrict__ out, int Hq, int max_ctx, int nc_stride, int fixed_chunk, int splits) {
+  __shared__ float wsh[ACOMB_MAXC];
+  __shared__ float lsh[ACOMB_MAXC];
+  __shared__ float red[2];
   const int d = threadIdx.x;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -213,25 +238,54 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(
     return;
   }
   const int C = chunk_len(L, fixed_chunk, splits);
-  const int nc = (L + C - 1) / C;
+  const int nc = min((L + C - 1) / C, ACOMB_MAXC);
   const float* pp = part + ((size_t)b * Hq + h) * nc_stride * APART;
+  // M* = max_c m_c
   float mx = -INFINITY;
-  for (int c = 0; c < nc; ++c) mx = fmaxf(mx, pp[c * APART]);
+  for (int cc = d; cc < nc; cc += 128) {
+    const float mc = pp[(size_t)cc * APART];
+    wsh[cc] = mc;
+    lsh[cc] = pp[(size_t)cc * APART + 1];
+    mx = fmaxf(mx, mc);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if ((d & 63) == 0) red[d >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(red[0], red[1]);
+  // w_c = exp(m_c - M*)
+  for (int cc = d; cc < nc; cc += 128) wsh[cc] = __expf(wsh[cc] - mx);
+  __syncthreads();
+  // Lsum and O_d in chunk order
   float ls = 0.0f, acc = 0.0f;
-  for (int c = 0; c < nc; ++c) {
-    const float w = __expf(pp[c * APART] - mx);
-    ls = __fmaf_rn(pp[c * APART + 1], w, ls);
-    acc = __fmaf_rn(pp[c * APART + 4 + d], w, acc);
+  const float* pd = pp + 4 + d;
+  int cc = 0;
+  for (; cc + 16 <= nc; cc += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = pd[(size_t)(cc + u) * APART];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      ls = __fmaf_rn(lsh[cc + u], wsh[cc + u], ls);
+      acc = __fmaf_rn(v[u], wsh[cc + u], acc);
+    }
+  }
+  for (; cc < nc; ++cc) {
+    ls = __fmaf_rn(lsh[cc], wsh[cc], ls);
+    acc = __fmaf_rn(pd[(size_t)cc * APART], wsh[cc], acc);
   }
   o[d] = (uint16_t)f32_to_bf16_bits(acc / ls);  // IEEE division
 }
 
+// Split count of the fast twin: enough (request, kv head, split) units for
+// four per CU, but never a chunk longer than the kernel's LDS holds.
 static int attn_splits(const bi_attn_desc* d, int num_cus) {
   const long long units = (long long)d->batch * d->num_kv_heads;
   long long s = (4LL * num_cus + units - 1) / units;
   const long long maxs = (d->max_ctx_len + ATILE - 1) / ATILE;
-  s = std::max(1LL, std::min(s, maxs));
-  return (int)s;
+  const long long mins = (d->max_ctx_len + ACH - 1) / ACH;
+  s = std::max(mins, std::min(s, maxs));
+  return (int)std::max(1LL, std::min(s, (long long)ACOMB_MAXC));
 }
 
 static int nc_stride_of(const bi_attn_desc* d, bool fast, int num_cus) {
