@@ -10,7 +10,7 @@
 //   chunk c = tokens [256c, 256c + 256) of the request, one workgroup per
 //   (chunk, kv head, request); inside it, tiles of 64 tokens in order with an
 //   online softmax per q head:
-//     s_t   = (sum_d q_d k_td, left to right) * scale
+//     s_t   = (sum_d q_d k_td, dims in order, pairs fused by v_dot2_f32_bf16) * scale
 //     m'    = max(m, max_t s_t);  alpha = exp(m - m') (0 while m = -inf)
 //     l     = l * alpha, then l = l + p_t in token order, p_t = exp(s_t - m')
 //     acc_d = acc_d * alpha, then acc_d = fma(p_t, v_td, acc_d) in token order
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens,
     float* __restrict__ part, int Hq, int Hkv, int max_blocks, long long num_pages, int max_ctx,
     int nc_stride, int fixed_chunk, int splits, float scale) {
-  __shared__ __attribute__((aligned(16))) float qs[G][AD];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[G][AD];
   __shared__ __attribute__((aligned(16))) uint16_t ks[ATILE * AKLD];
   __shared__ __attribute__((aligned(16))) uint16_t vs[ATILE * AD];
   __shared__ __attribute__((aligned(16))) float ps[G][ATILE];
@@ -72,9 +72,9 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
   const int t_end = min(L, t_begin + C);
   const int32_t* bt = block_table + (size_t)b * max_blocks;
 
-  // q of this kv head's G query heads, widened to fp32.
+  // q of this kv head's G query heads (bf16, as stored).
   for (int i = tid; i < G * AD; i += 256)
-    qs[i / AD][i % AD] = bf16_to_f32(q[((size_t)b * Hq + hk * G) * AD + i]);
+    qs[i / AD][i % AD] = q[((size_t)b * Hq + hk * G) * AD + i];
 
   // K/V tile loader: 64 tokens x 16 chunks of 16 B for each of K and V;
   // chunk ci = tid + 256 i: token ci/16, dims 8*(ci%16)..+7.
@@ -137,21 +137,15 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
         // scores: lane = token
         float s = -INFINITY;
         if (lane < nt) {
+          // q.k in dimension order, two dimensions per v_dot2_f32_bf16
           float dot = 0.0f;
           const uint16_t* krow = ks + lane * AKLD;
 #pragma unroll 4
           for (int d0 = 0; d0 < AD; d0 += 8) {
-            const u32x4_t kv8 = *(const u32x4_t*)(krow + d0);
-            const f32x4_t qa = *(const f32x4_t*)&qs[hh][d0];
-            const f32x4_t qb = *(const f32x4_t*)&qs[hh][d0 + 4];
-            dot = dot + qa[0] * bf16_lo(kv8[0]);
-            dot = dot + qa[1] * bf16_hi(kv8[0]);
-            dot = dot + qa[2] * bf16_lo(kv8[1]);
-            dot = dot + qa[3] * bf16_hi(kv8[1]);
-            dot = dot + qb[0] * bf16_lo(kv8[2]);
-            dot = dot + qb[1] * bf16_hi(kv8[2]);
-            dot = dot + qb[2] * bf16_lo(kv8[3]);
-            dot = dot + qb[3] * bf16_hi(kv8[3]);
+            const u32x4_t k8 = *(const u32x4_t*)(krow + d0);
+            const u32x4_t q8 = *(const u32x4_t*)&qs[hh][d0];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) dot = dot2_bf16(q8[w], k8[w], dot);
           }
           s = dot * scale;
         }

@@ -40,6 +40,13 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t& a, const u32x4_t&
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// acc + a.lo*b.lo + a.hi*b.hi for two packed bf16 pairs (v_dot2_f32_bf16).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
 // LDS transpose read of 16-bit data.  Within each group of 16 lanes, lane
 // 4r + c passes the address of 4 consecutive elements (row r, columns
 // 4c..4c+3) of a 4x16 block; afterwards lane i of the group holds column i

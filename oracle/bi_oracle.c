@@ -333,8 +333,10 @@ int or_rmsnorm_exact(const uint16_t *x, const uint16_t *g, double *y,
  *     M* = max_c m_c, w_c = exp(m_c - M*),
  *     Lsum = fma(l_c, w_c, Lsum) and O_d = fma(acc_c,d, w_c, O_d), c = 0..,
  *     out_d = bf16(O_d / Lsum).
- * Parity: bit-exact except the exponential (host expf vs the device's own
- * exp); unpinned at that level, covered by the tolerance.  Pinned by fp64
+ * Parity: the exponential (host expf vs the device's own exp) and the
+ * grouping inside the q.k dot (the device fuses dimension pairs with one
+ * dot-product instruction) are unpinned at the last-bit level and covered by
+ * the tolerance; everything else follows the same steps.  Pinned by fp64
  * brute force, the one-token case (out = v_0 exactly), constant V, q = 0,
  * and page-layout invariance.
  */
