@@ -72,15 +72,29 @@ __device__ __forceinline__ void stg128(void* p, const u32x4_t& v) { *(u32x4_t*)p
 // Direct-to-LDS load: every lane fetches 16 bytes at byte offset `off` of the
 // buffer; lane i's bytes land at lds_base + 16 i.  Reads past the end of the
 // buffer deposit zeros.  Completion is counted by vmcnt, not by any register.
-__device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (BI_LDS void*)lds_base, 16, off, 0, 0, 0);
+// Raw buffer resource as four dwords (base, stride 0, byte size, flags), for
+// inline assembly operands.  Offsets at or past `bytes` read as zero.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return i32x4_t{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
 
-// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained), N < 16.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+// Direct-to-LDS load of 16 bytes per lane: lane i's 16 bytes from byte offset
+// voff land at LDS byte address lds_addr + 16 i (lds_addr wave-uniform).
+// Issued from inline assembly so that the compiler's counter tracking does
+// not see it: the caller waits (s_waitcnt vmcnt) before the data is read.
+// M0, which the instruction takes the LDS address from, is restored.
+__device__ __forceinline__ void lds_dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "memory");
 }
 
 }  // namespace bi

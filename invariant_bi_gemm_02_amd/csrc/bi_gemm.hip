@@ -10,27 +10,36 @@
 // in the fixed index order, with no float atomics anywhere; the K split is
 // the same whatever M is, and the M tile is padded rather than re-chosen.
 //
-// Two kernels implement that schedule; which one runs depends on M, and the
-// bits never do (both issue the same matrix-core instruction on the same
-// operands in the same order, start every segment from +0, and fold the
-// segments with the same fp32 adds):
-//   gemm_split_kernel  small M (weight streaming, HBM bound): one workgroup
-//                      per (64-column tile, segment, 64-row tile); segment
-//                      sums go to an fp32 workspace; the last workgroup of a
-//                      tile to arrive (integer ticket) folds them in order.
-//   gemm_tile_kernel   large M (matrix-core bound): 128x128 output tiles, all
-//                      segments of K in one workgroup, folded in registers.
-// Padding rows (>= M) load as zero, are never stored, and 16-row sub-tiles
-// that are entirely padding skip their matrix-core ops.
+// Several kernels implement that schedule; which ones run depends on (M, N),
+// and the bits never do (all issue the same matrix-core instruction on the
+// same operands in the same order, start every segment from +0, and fold the
+// segments with the same fp32 adds in index order):
+//   gemm_skinny_kernel  M <= 16 (weight streaming, HBM bound): one 512-lane
+//                       workgroup per 64-column tile; with enough tiles to
+//                       fill the chip it streams all segments and folds them
+//                       in registers, otherwise one workgroup per (tile,
+//                       segment) writes the segment sum to the workspace.
+//   gemm_split_kernel   16 < M <= 64: one workgroup per (64-column tile,
+//                       segment, 64-row tile), segment sums to the workspace.
+//   gemm_fold_kernel    adds workspace segment sums in index order, narrows.
+//   gemm_tile_kernel    M > 64 (matrix-core bound): 256x128 output tiles, all
+//                       segments folded in registers; with too few tiles to
+//                       fill the chip, one workgroup per (tile, segment)
+//                       writes segment sums for gemm_fold_kernel instead.
+// Padding rows (>= M) load as zero through the buffer range check and are
+// never stored.
 //
 // W is [K,N] row-major (N contiguous), while the matrix core wants 8
 // consecutive K per lane for the B operand.  W tiles are therefore staged in
 // LDS as they sit in memory and read back with the LDS transpose read
 // (ds_read_b64_tr_b16), which hands each lane one column.
 //
-// The fast twin reuses both kernels with a schedule picked from M and the CU
-// count: the split kernel with a K slice sized to fill the chip, and the tile
-// kernel with a single accumulation chain over all of K (no segments).
+// The fast twin reuses these kernels with a schedule picked from M and the
+// CU count: at M > 64 the tile kernel runs one accumulation chain over all of
+// K (no segments), sliced in K only as far as needed to fill the chip; at
+// M <= 64 it runs the invariant kernels unchanged.
+#include <type_traits>
+
 #include "bi_common.h"
 #include "bi_internal.h"
 
@@ -305,249 +314,107 @@ __global__ __launch_bounds__(64) void gemm_fold_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Tile kernel (large M)
-// ---------------------------------------------------------------------------
-static constexpr int TBM = 128, TBN = 128, TBK = 64;
-static constexpr int T_LDX = TBK + 8;    // padded x row in LDS (elements)
-static constexpr int T_LDW = TBN + 16;   // padded W row in LDS (elements)
-
-// grid = (N/128, ceil(M/128)), block = 256: waves in a 2x2 grid, 64x64 each.
-// FOLD: true  -> segments of KC from +0, folded in registers (invariant);
-//       false -> one accumulation chain over all of K (fast twin).
-template <bool FOLD>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, uint16_t* __restrict__ y,
-    int M, int N, int K, int KC) {
-  __shared__ __attribute__((aligned(16))) uint16_t xl[2][TBM * T_LDX];
-  __shared__ __attribute__((aligned(16))) uint16_t wl[2][TBK * T_LDW];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * TBN;
-  const int m0 = blockIdx.y * TBM;
-
-  // Loaders: x stage 128 rows x 64 K (8 chunks per row), W stage 64 rows x
-  // 128 columns (16 chunks per row); 4 chunks of 16 B per thread for each.
-  u32x4_t xr[4], wr[4];
-  auto load_stage = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c >> 3, kc = c & 7;
-      const int m = m0 + r;
-      if (m < M && k0 + kc * 8 < K)
-        xr[i] = ldg128(x + (size_t)m * K + k0 + kc * 8);
-      else
-        xr[i] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c >> 4, nc = c & 15;
-      const int k = k0 + r;
-      if (k < K && n0 + nc * 8 < N)
-        wr[i] = ldg128(W + (size_t)k * N + n0 + nc * 8);
-      else
-        wr[i] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      *(u32x4_t*)&xl[buf][(c >> 3) * T_LDX + (c & 7) * 8] = xr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      *(u32x4_t*)&wl[buf][(c >> 4) * T_LDW + (c & 15) * 8] = wr[i];
-    }
-  };
-
-  f32x4_t acc[4][4];
-  f32x4_t tot[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      tot[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-
-  // 16-row sub-tiles of this wave that hold at least one row < M.
-  const int wrow0 = m0 + wm * 64;
-  const int nsub = max(0, min(4, (M - wrow0 + 15) >> 4));
-
-  const int g = lane >> 4;
-  const int tr_r = (lane & 15) >> 2;
-  const int tr_c = lane & 3;
-  const int arow = lane & 15;
-
-  const int nstage = (K + TBK - 1) / TBK;
-  const int blocks_per_seg = KC / KB;
-  int seg = 0;
-  int kblk_in_seg = 0;
-
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int st = 0; st < nstage; ++st) {
-    const int k0 = st * TBK;
-    if (st + 1 < nstage) load_stage(k0 + TBK);
-    const uint16_t* xs = xl[st & 1];
-    const uint16_t* ws = wl[st & 1];
-    const int nkb = min(TBK, K - k0) / KB;
-    for (int j = 0; j < nkb; ++j) {
-      u32x4_t bf[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint16_t* base = ws + (j * KB + 8 * g + tr_r) * T_LDW + wn * 64 + t * 16 + 4 * tr_c;
-        const u32x2_t b0 = lds_read_tr16(base);
-        const u32x2_t b1 = lds_read_tr16(base + 4 * T_LDW);
-        bf[t] = u32x4_t{b0.x, b0.y, b1.x, b1.y};
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (s < nsub) {
-          const u32x4_t af =
-              *(const u32x4_t*)&xs[(wm * 64 + s * 16 + arow) * T_LDX + j * KB + g * 8];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[s][t] = mfma16x16x32(af, bf[t], acc[s][t]);
-        }
-      }
-      if (FOLD) {
-        // segment boundary: fold this segment's sum into the running total
-        if (++kblk_in_seg == blocks_per_seg || (k0 + (j + 1) * KB) >= K) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              if (seg == 0)
-                tot[s][t] = acc[s][t];
-              else
-                tot[s][t] = tot[s][t] + acc[s][t];
-              acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
-          ++seg;
-          kblk_in_seg = 0;
-        }
-      }
-    }
-    if (st + 1 < nstage) store_stage((st + 1) & 1);
-    __syncthreads();
-  }
-
-  // Epilogue: narrow and store rows < M.
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (s < nsub) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int col = n0 + wn * 64 + t * 16 + (lane & 15);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = wrow0 + s * 16 + (lane >> 4) * 4 + e;
-          const float v = FOLD ? tot[s][t][e] : acc[s][t][e];
-          if (m < M && col < N) y[(size_t)m * N + col] = (uint16_t)f32_to_bf16_bits(v);
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Tile kernel v3 (large M, matrix-core bound)
+// Tile kernel (large M, matrix-core bound)
 // ---------------------------------------------------------------------------
 // 256 x 128 output tile per workgroup of 8 waves (4 x 2), each wave 64 x 64
 // (4 x 4 matrix-core tiles), two waves per SIMD.  K advances in stages of 64
-// (two K-blocks): the next stage's x slab (256 x 64) and W slab (64 x 128)
-// are fetched into registers while the current stage is multiplied out of
-// LDS, then written to the other of two LDS stage buffers.  LDS rows are
-// XOR-swizzled in 16-byte chunks so that the A-operand reads (8 rows at a
-// time) and the transpose reads of W (4 rows at a time) hit distinct banks.
-// FOLD: segments of KC from +0 folded in order in registers (batch-invariant
-// schedule); without FOLD one accumulation chain runs over all of K.
-// Workgroups are mapped to tiles so that each XCD (workgroups are dispatched
-// to the 8 XCDs round robin) works on a contiguous band of tiles, m fastest:
-// workgroups sharing an L2 share W column panels and x row panels.
-static constexpr int T2_BN = 128, T2_BK = 64;
-static constexpr int T2_WS = T2_BK * T2_BN;          // W slab elements (16 KB)
+// (two K-blocks) through a ring of three LDS stage buffers (48 KB each) that
+// direct-to-LDS buffer loads fill three stages ahead; one barrier per stage.
+// Fragments are read one K-block ahead, across stage boundaries.
+//
+// LDS layout of a stage: the x slab (256 rows x 64 k, 128 B rows) then the W
+// slab (64 k-rows x 128 columns, 256 B rows), both in 16-B chunks whose index
+// is XORed with low row bits, so that the A-operand reads (16 rows, one chunk
+// each) and the transpose reads of W (16 k-rows, 32 B each) spread over all
+// LDS banks.  A direct-to-LDS load writes lane i at 16 i, so each lane
+// fetches the global chunk whose swizzled home is its slot.
+//
+// Each 16x16 product is issued as y^T = W^T x^T (W fragment as the A operand):
+// the same products in the same order as x W, with the accumulator holding
+// four consecutive columns of one row per lane, which makes the stores 8 B.
+//
+// FOLD: segments of KC (a multiple of 64) from +0, folded in order into the
+// running total after each (batch-invariant schedule); the first K-block of
+// a segment is issued with a zero accumulator.  Without FOLD, one chain runs
+// over the workgroup's K range.  SLICE: the workgroup covers only K slice
+// blockIdx.y ([y*KC, y*KC + KC)) and writes its fp32 sum to part[y][M][N].
+//
+// Workgroups are dispatched to the 8 XCDs round robin.  remap 2 gives each
+// XCD a band of whole tile columns, walked in groups of 4 tile rows, so that
+// the 32 workgroups an XCD runs at once share 4 x panels and 8 W panels in
+// its L2; remap 1 gives each XCD a contiguous band of tiles, m fastest.
+static constexpr int TL_BM = 256, TL_BN = 128, TL_BK = 64;
+static constexpr int TL_XS = TL_BM * TL_BK;             // x slab elements (32 KB)
+static constexpr int TL_STAGE = TL_XS + TL_BK * TL_BN;  // + W slab (16 KB)
 
-// element offset of logical 16-B chunk `c` of row `r` in the x slab (8 chunks per row)
-__device__ __forceinline__ int t2_xphys(int r, int c) { return r * T2_BK + ((c ^ (r & 7)) << 3); }
-// element offset of logical 16-B chunk `c` of k-row `r` in the W slab (16 chunks
-// per row), which follows an x slab of `xs` elements
-__device__ __forceinline__ int t2_wphys(int xs, int r, int c) {
-  return xs + r * T2_BN + ((c ^ ((r & 3) << 1)) << 3);
+__device__ __forceinline__ int tl_xphys(int r, int c) { return r * TL_BK + ((c ^ (r & 7)) << 3); }
+__device__ __forceinline__ int tl_wswz(int r) { return ((r & 3) << 1) ^ (((r >> 3) & 1) << 3); }
+__device__ __forceinline__ int tl_wphys(int r, int c) {
+  return TL_XS + r * TL_BN + ((c ^ tl_wswz(r)) << 3);
 }
 
-// BM rows per workgroup, 2*BM lanes (BM/64 x 2 waves of 64 x 64).  256 is the
-// size in use: with the fold's second set of accumulators, 128 spills.
-// SLICE: the workgroup covers only K slice blockIdx.y ([y*KC, y*KC + KC)),
-// accumulated in one chain from +0, and writes the fp32 slice sum to
-// part[y][M][N] for gemm_fold_kernel (used when the tiles alone are too few
-// to fill the chip; with KC = 512 the slice is exactly one segment).
-template <bool FOLD, int BM, bool SLICE = false>
-__global__ __launch_bounds__(BM * 2, 2) void gemm_tile2_kernel(
+template <bool FOLD, bool SLICE>
+__global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, uint16_t* __restrict__ y,
-    int M, int N, int K, int KC, int tm, int tn, int remap, float* __restrict__ part = nullptr) {
-  constexpr int NT = BM * 2;                  // lanes per workgroup
-  constexpr int T2_BM = BM;
-  constexpr int T2_XS = BM * T2_BK;           // x slab elements
-  constexpr int T2_STAGE = T2_XS + T2_WS;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][T2_STAGE];
+    int M, int N, int K, int KC, int tm, int tn, int remap, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * TL_STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int g = lane >> 4;
   const int l16 = lane & 15;
   const int tr_r = l16 >> 2, tr_c = lane & 3;
 
   int t = blockIdx.x;
-  if (remap) t = (t & 7) * ((tm * tn) >> 3) + (t >> 3);
-  const int m0 = (t % tm) * T2_BM;
-  const int n0 = (t / tm) * T2_BN;
+  if (remap == 1) {
+    t = (t & 7) * ((tm * tn) >> 3) + (t >> 3);
+  } else if (remap == 2) {
+    const int ncols = tn >> 3, xcd = t & 7, i = t >> 3;
+    const int first = (i / (4 * ncols)) * 4, gm = min(4, tm - first);
+    const int r = i - first * ncols;
+    t = (xcd * ncols + r / gm) * tm + first + r % gm;
+  }
+  const int m0 = (t % tm) * TL_BM;
+  const int n0 = (t / tm) * TL_BN;
 
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)((size_t)K * N * 2));
-  // K range of this workgroup: all of K, or one slice
+  const i32x4_t xr = make_rsrc_words(x, (uint32_t)((size_t)M * K * 2));
+  const i32x4_t wr = make_rsrc_words(W, (uint32_t)((size_t)K * N * 2));
   const int kbeg = SLICE ? (int)blockIdx.y * KC : 0;
   const int kend = SLICE ? min(K, kbeg + KC) : K;
+  const int nstage = (kend - kbeg + TL_BK - 1) / TL_BK;
 
-  // Loads of one stage: x chunks c = tid + NT i (row c/8, chunk c%8), W
-  // chunks c = tid + NT i (k-row c/16, chunk c%16).  Rows >= M and k >= K
-  // read as zero through the buffer range check.
-  constexpr int XL = T2_XS / 8 / NT;          // 16-B x chunks per lane per stage (4)
-  constexpr int WL = T2_WS / 8 / NT;          // 16-B W chunks per lane per stage (2 or 4)
-  const uint32_t xoff0 = (uint32_t)((m0 + (tid >> 3)) * K + (tid & 7) * 8) * 2;
-  const uint32_t xrowstep = (uint32_t)K * 2 * (NT / 8);    // NT/8 rows of x, in bytes
-  const uint32_t woff0 = (uint32_t)((tid >> 4) * N + n0 + (tid & 15) * 8) * 2;
-  const uint32_t wrowstep = (uint32_t)N * 2 * (NT / 16);   // NT/16 k-rows of W, in bytes
-  u32x4_t xs[XL], ws[WL];
-  auto load_stage = [&](int k0) {
-    const bool valid = k0 < kend;   // past the end: zeros, no memory traffic
+  // Each wave instruction fills 1 KB of a stage: wave w fills x regions
+  // 4w..4w+3 (8 rows each) and W regions 2w, 2w+1 (4 k-rows each).
+  uint32_t xoff[4], woff[2];
 #pragma unroll
-    for (int i = 0; i < XL; ++i)
-      xs[i] = bufld128(xr, valid ? xoff0 + i * xrowstep + (uint32_t)k0 * 2 : 0x80000000u);
+  for (int i = 0; i < 4; ++i) {
+    const int p = (wave * 4 + i) * 64 + lane;
+    const int r = p >> 3, c = (p & 7) ^ (r & 7);
+    xoff[i] = ((uint32_t)(m0 + r) * (uint32_t)K + (uint32_t)(kbeg + c * 8)) * 2u;
+  }
 #pragma unroll
-    for (int i = 0; i < WL; ++i)
-      ws[i] = bufld128(wr, valid ? woff0 + i * wrowstep + (uint32_t)k0 * N * 2 : 0x80000000u);
-  };
-  auto store_stage = [&](uint16_t* buf) {
+  for (int i = 0; i < 2; ++i) {
+    const int p = (wave * 2 + i) * 64 + lane;
+    const int r = p >> 4, c = (p & 15) ^ tl_wswz(r);
+    woff[i] = ((uint32_t)(kbeg + r) * (uint32_t)N + (uint32_t)(n0 + c * 8)) * 2u;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(BI_LDS void*)lds;
+  // Loads of stage st.  Past the last stage they take an offset outside the
+  // buffer (zeros, no memory traffic), so every stage issues exactly six per
+  // wave and the counter waits below hold.  Rows >= M and k >= K read as zero.
+  auto dma = [&](int st) {
+    const bool valid = st < nstage;
+    const uint32_t base = lds0 + (uint32_t)((st % 3) * TL_STAGE * 2);
 #pragma unroll
-    for (int i = 0; i < XL; ++i) {
-      const int c = tid + NT * i;
-      *(u32x4_t*)(buf + t2_xphys(c >> 3, c & 7)) = xs[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      lds_dma16(xr, valid ? xoff[i] + (uint32_t)(st * TL_BK * 2) : 0x80000000u,
+                base + (uint32_t)((wave * 4 + i) * 1024));
 #pragma unroll
-    for (int i = 0; i < WL; ++i) {
-      const int c = tid + NT * i;
-      *(u32x4_t*)(buf + t2_wphys(T2_XS, c >> 4, c & 15)) = ws[i];
-    }
+    for (int i = 0; i < 2; ++i)
+      lds_dma16(wr, valid ? woff[i] + (uint32_t)(st * TL_BK) * (uint32_t)N * 2u : 0x80000000u,
+                base + (uint32_t)(TL_XS * 2 + (wave * 2 + i) * 1024));
   };
 
   f32x4_t acc[4][4];
@@ -556,115 +423,105 @@ __global__ __launch_bounds__(BM * 2, 2) void gemm_tile2_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // -0 + s == s exactly for every s, so the first fold copies the first
+  // segment's sum bit for bit
 #pragma unroll
   for (int i = 0; i < (FOLD ? 4 : 1); ++i)
 #pragma unroll
-    for (int j = 0; j < (FOLD ? 4 : 1); ++j) tot[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < (FOLD ? 4 : 1); ++j) tot[i][j] = f32x4_t{-0.f, -0.f, -0.f, -0.f};
 
-  const int wrow0 = m0 + wm * 64;
-  const int nsub = max(0, min(4, (M - wrow0 + 15) >> 4));
-  const int blocks_per_seg = KC / KB;
-  int kblk = 0;  // K-blocks done in the current segment
-  int seg = 0;
-
-  // LDS element offsets of this lane's operand reads for K-block 0 of a
-  // stage; sub-tile s adds 16 rows (the x swizzle uses row % 8, unchanged),
-  // K-block 1 adds 4 chunks (x) or 32 rows (W, swizzle uses row % 4).
-  int aoff[2], boff[4][2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) aoff[j] = t2_xphys(wm * 64 + l16, j * 4 + g);
+  // lane's element offsets within a stage (K-block 0)
+  const int aoff = tl_xphys(wm * 64 + l16, g);
+  int boff[4][2];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     const int col = wn * 64 + tt * 16 + 4 * tr_c;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      boff[tt][h] = t2_wphys(T2_XS, 8 * g + 4 * h + tr_r, col >> 3) + (col & 7);
+    for (int h = 0; h < 2; ++h) boff[tt][h] = tl_wphys(8 * g + 4 * h + tr_r, col >> 3) + (col & 7);
   }
 
-  // operand fragments of one K-block: A for the 4 sub-tiles, B for the 4 columns
   u32x4_t af[2][4], bf[2][4];
-  auto read_frags = [&](const uint16_t* buf, int j, int set) {
+  // fragments of K-block j (0 or 1) of stage st into set j
+  auto read_frags = [&](int st, int j) {
+    const uint16_t* buf = lds + (st % 3) * TL_STAGE;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      const u32x2_t b0 = lds_read_tr16(buf + boff[tt][0] + j * KB * T2_BN);
-      const u32x2_t b1 = lds_read_tr16(buf + boff[tt][1] + j * KB * T2_BN);
-      bf[set][tt] = u32x4_t{b0.x, b0.y, b1.x, b1.y};
+      const u32x2_t b0 = lds_read_tr16(buf + boff[tt][0] + j * KB * TL_BN);
+      const u32x2_t b1 = lds_read_tr16(buf + boff[tt][1] + j * KB * TL_BN);
+      bf[j][tt] = u32x4_t{b0.x, b0.y, b1.x, b1.y};
     }
+    // K-block 1 is logical chunk g + 4 of the row: the swizzle keeps bit 2
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      af[set][s] = *(const u32x4_t*)(buf + aoff[j] + s * 16 * T2_BK);
+      af[j][s] = *(const u32x4_t*)(buf + (j ? (aoff ^ 32) : aoff) + s * 16 * TL_BK);
   };
-  auto fold_if_segment_end = [&](int kdone) {
-    if (FOLD) {
-      if (++kblk == blocks_per_seg || kdone >= kend) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            if (seg == 0)
-              tot[s][tt] = acc[s][tt];
-            else
-              tot[s][tt] = tot[s][tt] + acc[s][tt];
-            acc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          }
-        ++seg;
-        kblk = 0;
-      }
-    }
-  };
-  // Multiply one stage: the fragments of K-block 1 are read while the
-  // multiplies of K-block 0 run.  Every 16-row sub-tile is multiplied,
-  // padding rows included (they hold zeros and are never stored).
-  auto compute = [&](const uint16_t* buf, int k0) {
-    read_frags(buf, 0, 0);
-    const bool two = k0 + KB < kend;
-    if (two) read_frags(buf, 1, 1);
+  auto mma = [&](int j, bool from_zero) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) acc[s][tt] = mfma16x16x32(af[0][s], bf[0][tt], acc[s][tt]);
-    fold_if_segment_end(k0 + KB);
-    if (two) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) acc[s][tt] = mfma16x16x32(af[1][s], bf[1][tt], acc[s][tt]);
-      fold_if_segment_end(k0 + 2 * KB);
-    }
+      for (int tt = 0; tt < 4; ++tt)
+        acc[s][tt] = mfma16x16x32(bf[j][tt], af[j][s],
+                                  from_zero ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[s][tt]);
   };
-  auto lds_barrier = [&]() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  auto fold = [&]() {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) tot[s][tt] = tot[s][tt] + acc[s][tt];
+  };
+  // One stage: K-block 0 (from +0 when it opens a segment), barrier, refill
+  // of the buffer just consumed, next stage's K-block 0 fragments, K-block 1.
+  auto stage = [&](int st, auto zero) {
+    const bool two = kbeg + st * TL_BK + KB < kend;
+    // read even when K-block 1 is past K (the fragments are then unused), so
+    // that the LDS-counter waits see one path
+    read_frags(st, 1);
+    // K-block 0's fragments (the 12 LDS reads before these 12) have arrived
+    __builtin_amdgcn_s_waitcnt(0xCC7F);  // lgkmcnt(12); vmcnt, expcnt unconstrained
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0, decltype(zero)::value);
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave's loads of stage st+1 have landed (only stage st+2's six may
+    // be in flight) and its reads of stage st are done; after the barrier
+    // every wave's are, so stage st's buffer can be refilled
+    asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    dma(st + 3);
+    read_frags(st + 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (two) mma(1, false);
   };
 
-  const int nstage = (kend - kbeg + T2_BK - 1) / T2_BK;
-  load_stage(kbeg);
-  store_stage(lds[0]);
-  lds_barrier();
-  for (int st = 0; st < nstage; ++st) {
-    load_stage(kbeg + (st + 1) * T2_BK);
-    compute(lds[st & 1], kbeg + st * T2_BK);
-    if (st + 1 < nstage) store_stage(lds[(st + 1) & 1]);
-    lds_barrier();
+  dma(0);
+  dma(1);
+  dma(2);
+  asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+  read_frags(0, 0);
+  const int sps = FOLD ? KC / TL_BK : nstage;  // stages per segment
+  int st = 0;
+  for (;;) {
+    stage(st, std::true_type{});
+    const int seg_end = min(nstage, st + sps);
+    for (++st; st < seg_end; ++st) stage(st, std::false_type{});
+    if (st >= nstage) break;
+    fold();
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (FOLD) fold();
 
+  const int wrow0 = m0 + wm * 64;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    if (s < nsub) {
+    const int m = wrow0 + s * 16 + l16;
+    if (m < M && n0 + wn * 64 < N) {  // N is a multiple of 64: a wave's columns are all in or out
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const int col = n0 + wn * 64 + tt * 16 + l16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = wrow0 + s * 16 + g * 4 + e;
-          const float v = FOLD ? tot[s][tt][e] : acc[s][tt][e];
-          if (m < M && col < N) {
-            if (SLICE)
-              part[((size_t)blockIdx.y * M + m) * N + col] = v;
-            else
-              y[(size_t)m * N + col] = (uint16_t)f32_to_bf16_bits(v);
-          }
+        const f32x4_t v = FOLD ? tot[s][tt] : acc[s][tt];
+        const int col = n0 + wn * 64 + tt * 16 + g * 4;
+        if (SLICE) {
+          *(f32x4_t*)&part[((size_t)blockIdx.y * M + m) * N + col] = v;
+        } else {
+          *(u32x2_t*)&y[(size_t)m * N + col] =
+              u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
       }
     }
@@ -675,7 +532,7 @@ __global__ __launch_bounds__(BM * 2, 2) void gemm_tile2_kernel(
 // Host side
 // ---------------------------------------------------------------------------
 static constexpr int BI_KC = 512;  // invariant segment length
-static constexpr int TILE_BM = 256;  // rows per tile-kernel workgroup (8 waves)
+static constexpr int TILE_BM = TL_BM;  // rows per tile-kernel workgroup (8 waves)
 static constexpr int SPLIT_MAX_M = 64;
 static constexpr int SKINNY_MAX_M = 16;
 static constexpr int SKINNY_ALLK_TILES = 256;  // 64-column tiles that fill the chip alone
@@ -688,7 +545,7 @@ static constexpr int TILE_MIN_TILES = 192;  // fewer tiles than this: split K in
 enum class GemmPath { Tile, TileSlice, SkinnyAllK, SkinnySeg, Split };
 static GemmPath gemm_path(int64_t M, int64_t N) {
   if (M > SPLIT_MAX_M)
-    return ceil_div(M, TILE_BM) * ceil_div(N, T2_BN) >= TILE_MIN_TILES ? GemmPath::Tile
+    return ceil_div(M, TILE_BM) * ceil_div(N, TL_BN) >= TILE_MIN_TILES ? GemmPath::Tile
                                                                          : GemmPath::TileSlice;
   if (M <= SKINNY_MAX_M) return (N / SK_BN >= SKINNY_ALLK_TILES) ? GemmPath::SkinnyAllK
                                                                   : GemmPath::SkinnySeg;
@@ -700,9 +557,9 @@ static GemmPath gemm_path(int64_t M, int64_t N) {
 // At M <= 64 the fast twin keeps the invariant kernels (their schedule is
 // already the fastest layout for streaming W).
 int64_t fast_split_kc(int64_t M, int64_t N, int64_t K, int num_cus) {
-  const int64_t tiles = ceil_div(M, TILE_BM) * ceil_div(N, T2_BN);
+  const int64_t tiles = ceil_div(M, TILE_BM) * ceil_div(N, TL_BN);
   const int64_t slices = std::max<int64_t>(1, ceil_div(std::max(num_cus, 1), tiles));
-  return ceil_div(ceil_div(K, slices), T2_BK) * T2_BK;
+  return ceil_div(ceil_div(K, slices), TL_BK) * TL_BK;
 }
 static int64_t slice_kc(int64_t M, int64_t N, int64_t K, bool fast, int num_cus) {
   return fast ? fast_split_kc(M, N, K, num_cus) : BI_KC;
@@ -719,30 +576,26 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
                 int64_t K, void* ws, size_t ws_bytes, hipStream_t stream, bool fast, int num_cus) {
   const int64_t S = ceil_div(K, BI_KC);
   const GemmPath p = gemm_path(M, N);
-  if (p == GemmPath::Tile) {
-    constexpr int BM = TILE_BM;
-    const int64_t tm = ceil_div(M, BM), tn = ceil_div(N, T2_BN);
-    const int remap = ((tm * tn) % 8 == 0) ? 1 : 0;
-    dim3 grid((unsigned)(tm * tn));
-    if (fast)
-      hipLaunchKernelGGL((gemm_tile2_kernel<false, BM>), grid, dim3(2 * BM), 0, stream, x, W, y,
-                         (int)M, (int)N, (int)K, (int)K, (int)tm, (int)tn, remap);
-    else
-      hipLaunchKernelGGL((gemm_tile2_kernel<true, BM>), grid, dim3(2 * BM), 0, stream, x, W, y,
-                         (int)M, (int)N, (int)K, BI_KC, (int)tm, (int)tn, remap);
-    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
-  }
-  if (p == GemmPath::TileSlice) {
-    constexpr int BM = TILE_BM;
+  if (p == GemmPath::Tile || p == GemmPath::TileSlice) {
+    const int64_t tm = ceil_div(M, TILE_BM), tn = ceil_div(N, TL_BN);
+    const int remap = (tn % 8 == 0) ? 2 : ((tm * tn) % 8 == 0) ? 1 : 0;
+    if (p == GemmPath::Tile) {
+      dim3 grid((unsigned)(tm * tn));
+      if (fast)
+        hipLaunchKernelGGL((gemm_tile_kernel<false, false>), grid, dim3(512), 0, stream, x, W, y,
+                           (int)M, (int)N, (int)K, (int)K, (int)tm, (int)tn, remap, (float*)nullptr);
+      else
+        hipLaunchKernelGGL((gemm_tile_kernel<true, false>), grid, dim3(512), 0, stream, x, W, y,
+                           (int)M, (int)N, (int)K, BI_KC, (int)tm, (int)tn, remap, (float*)nullptr);
+      return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+    }
     const int64_t kc = slice_kc(M, N, K, fast, num_cus);
     const int64_t ns = ceil_div(K, kc);
-    const int64_t tm = ceil_div(M, BM), tn = ceil_div(N, T2_BN);
     if (ns > 65535) return BI_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < (size_t)ns * (size_t)M * (size_t)N * sizeof(float)) return BI_ERR_WORKSPACE;
     float* part = (float*)ws;
-    const int remap = ((tm * tn) % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((gemm_tile2_kernel<false, BM, true>), dim3((unsigned)(tm * tn), (unsigned)ns),
-                       dim3(2 * BM), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)kc, (int)tm,
+    hipLaunchKernelGGL((gemm_tile_kernel<false, true>), dim3((unsigned)(tm * tn), (unsigned)ns),
+                       dim3(512), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)kc, (int)tm,
                        (int)tn, remap, part);
     if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
     hipLaunchKernelGGL(gemm_fold_kernel, dim3((unsigned)ceil_div(N, 256), (unsigned)M), dim3(64),
