@@ -236,7 +236,7 @@ def main():
         ach = gemm_flops(M, K_gu, N_gu) / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": None,
-                "kernel": "gemm_tile2_kernel<true> (gate_up 4096->28672)",
+                "kernel": "gemm_tile_kernel<true, false> (gate_up 4096->28672)",
                 "avg_launch_us": gu_ms * 1e3}
     else:
         ach = gemm_bytes(M, K_gu, N_gu) / (gu_ms * 1e-3) / 1e9
