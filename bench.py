@@ -242,7 +242,7 @@ def main():
         ach = gemm_bytes(M, K_gu, N_gu) / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                "kernel": "gemm_skinny_kernel<true> (gate_up 4096->28672)",
+                "kernel": "gemm_skinny_kernel + gemm_fold_kernel (gate_up 4096->28672)",
                 "avg_launch_us": gu_ms * 1e3}
 
     roof["traffic"] = measured_traffic(M)

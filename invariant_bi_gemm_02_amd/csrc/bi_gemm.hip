@@ -14,13 +14,9 @@
 // and the bits never do (all issue the same matrix-core instruction on the
 // same operands in the same order, start every segment from +0, and fold the
 // segments with the same fp32 adds in index order):
-//   gemm_skinny_kernel  M <= 16 (weight streaming, HBM bound): one 512-lane
-//                       workgroup per 64-column tile; with enough tiles to
-//                       fill the chip it streams all segments and folds them
-//                       in registers, otherwise one workgroup per (tile,
-//                       segment) writes the segment sum to the workspace.
-//   gemm_split_kernel   16 < M <= 64: one workgroup per (64-column tile,
-//                       segment, 64-row tile), segment sums to the workspace.
+//   gemm_skinny_kernel  M <= 64 (weight streaming, HBM bound): one 512-lane
+//                       workgroup per (64-column tile, segment) writes the
+//                       segment sum to the workspace.
 //   gemm_fold_kernel    adds workspace segment sums in index order, narrows.
 //   gemm_tile_kernel    M > 64 (matrix-core bound): 256x128 output tiles, all
 //                       segments folded in registers; with too few tiles to
@@ -46,157 +42,36 @@
 namespace bi {
 
 static constexpr int KB = 32;        // K per matrix-core op
-static constexpr int SPLIT_BN = 64;  // columns per split workgroup (4 waves x 16)
-static constexpr int SPLIT_BM = 64;  // rows per split workgroup (4 sub-tiles of 16)
-static constexpr int SPLIT_SK = 128; // K rows of W staged per LDS buffer
-static constexpr int SPLIT_LDW = SPLIT_BN + 16;  // padded LDS row (elements)
 
 // ---------------------------------------------------------------------------
-// Split kernel (small M)
+// Skinny kernel (M <= 64, the decode regime: W streamed once, HBM bound)
 // ---------------------------------------------------------------------------
-// grid = (N/64, S, ceil(M/64)), block = 256 (4 waves).  Wave w owns columns
-// n0 + 16w .. +15 of the tile and every 16-row sub-tile that holds a row < M.
-// Per stage of 128 K: the W slab (128 x 64) goes through LDS, the x
-// fragments stay in registers; the next stage is fetched while this one runs.
-// MAXSUB = 1 for M <= 16 (fewer registers), 4 otherwise.
-template <int MAXSUB>
-__global__ __launch_bounds__(256) void gemm_split_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
-    float* __restrict__ part, int M, int N, int K, int KC) {
-  __shared__ __attribute__((aligned(16))) uint16_t wl[2][SPLIT_SK * SPLIT_LDW];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int ntile = blockIdx.x;
-  const int seg = blockIdx.y;
-  const int mtile = blockIdx.z;
-  const int n0 = ntile * SPLIT_BN;
-  const int m0 = mtile * SPLIT_BM;
-  const int k_begin = seg * KC;
-  const int k_end = min(K, k_begin + KC);
-  const int rows = min(SPLIT_BM, M - m0);
-  const int nsub = min(MAXSUB, (rows + 15) >> 4);  // 16-row sub-tiles holding a real row
-
-  // A operand lanes: row m0 + 16*sub + lane%16, k = kb + (lane/16)*8 .. +7.
-  const int arow = lane & 15;
-  const int g = lane >> 4;
-  // B operand via transpose read: lane 4r+c of group g addresses row
-  // kb + 8g + 4h + r, columns 16*wave + 4c .. +3, for h = 0, 1.
-  const int tr_r = (lane & 15) >> 2;
-  const int tr_c = lane & 3;
-
-  u32x4_t wreg[4];
-  u32x4_t acur[MAXSUB][4], anext[MAXSUB][4];
-  // One stage: W rows k0..k0+127 (chunk c = tid + 256 i: row c/8, columns
-  // 8*(c%8)..+7) and the x fragments of its four K-blocks.
-  auto load_stage = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int k = k0 + (c >> 3);
-      wreg[i] = (k < k_end) ? ldg128(W + (size_t)k * N + n0 + (c & 7) * 8)
-                            : u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int s = 0; s < MAXSUB; ++s) {
-      const int m = m0 + s * 16 + arow;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kb = k0 + j * KB;
-        anext[s][j] = (s < nsub && m < M && kb < k_end) ? ldg128(x + (size_t)m * K + kb + g * 8)
-                                                         : u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_w = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      *(u32x4_t*)&wl[buf][(c >> 3) * SPLIT_LDW + (c & 7) * 8] = wreg[i];
-    }
-  };
-
-  f32x4_t acc[MAXSUB];
-#pragma unroll
-  for (int s = 0; s < MAXSUB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nstage = (k_end - k_begin + SPLIT_SK - 1) / SPLIT_SK;
-  load_stage(k_begin);
-  store_w(0);
-#pragma unroll
-  for (int s = 0; s < MAXSUB; ++s)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acur[s][j] = anext[s][j];
-  __syncthreads();
-  for (int st = 0; st < nstage; ++st) {
-    const int k0 = k_begin + st * SPLIT_SK;
-    if (st + 1 < nstage) load_stage(k0 + SPLIT_SK);
-    const uint16_t* wb = wl[st & 1];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (k0 + j * KB < k_end) {
-        const uint16_t* base = wb + (j * KB + 8 * g + tr_r) * SPLIT_LDW + 16 * wave + 4 * tr_c;
-        const u32x2_t b0 = lds_read_tr16(base);
-        const u32x2_t b1 = lds_read_tr16(base + 4 * SPLIT_LDW);
-        const u32x4_t bfrag = u32x4_t{b0.x, b0.y, b1.x, b1.y};
-#pragma unroll
-        for (int s = 0; s < MAXSUB; ++s)
-          if (s < nsub) acc[s] = mfma16x16x32(acur[s][j], bfrag, acc[s]);
-      }
-    }
-    if (st + 1 < nstage) {
-      store_w((st + 1) & 1);
-#pragma unroll
-      for (int s = 0; s < MAXSUB; ++s)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acur[s][j] = anext[s][j];
-    }
-    __syncthreads();
-  }
-
-  // Segment partial -> workspace part[seg][m][n] (rows < M only).
-  const int ccol = n0 + 16 * wave + (lane & 15);
-#pragma unroll
-  for (int s = 0; s < MAXSUB; ++s) {
-    if (s < nsub) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + s * 16 + g * 4 + e;
-        if (m < M) part[((size_t)seg * M + m) * N + ccol] = acc[s][e];
-      }
-    }
-  }
-
-}
-
-// ---------------------------------------------------------------------------
-// Skinny kernel (M <= 16, the decode regime: W streamed once, HBM bound)
-// ---------------------------------------------------------------------------
-// One workgroup of 512 lanes owns a 64-column tile of y (128-byte rows of W,
-// so every W line fetched is used whole) and either
-//   ALLK = false: one 512-row segment of K; its sum goes to the workspace and
-//                 gemm_fold_kernel adds the segments in order afterwards, or
-//   ALLK = true:  every segment of K in order, folded in registers, y written
-//                 directly (used when the 64-column tiles alone fill the chip).
-// The whole 64 KB W slab of a segment is requested at once (8 loads of 16 B
-// per lane) and the next segment's slab is in flight while the current one
-// is multiplied.  The slab sits in LDS with its 16-byte chunks XOR-swizzled
-// by row, so the transpose reads of four consecutive rows hit distinct banks.
-// Waves 0..3 each own one 16-column sub-tile; x fragments come straight from
-// memory (rows >= M read as zero through the buffer range check).
+// One workgroup of 512 lanes per (64-column tile, 512-row segment of K):
+// 128-byte rows of W, so every W line fetched is used whole.  The segment's
+// sum goes to the workspace and gemm_fold_kernel adds the segments in order.
+// The whole 64 KB W slab is requested at once (8 loads of 16 B per lane),
+// then the x slab (16 MT rows, padded: rows >= M read as zero through the
+// buffer range check).  Both sit in LDS with 16-byte chunks XOR-swizzled by
+// row, so the transpose reads of W (4 consecutive rows) and the A-operand
+// reads of x (16 rows, same chunk) hit distinct banks.  The 4 x MT
+// matrix-core chains (16-column group, 16-row sub-tile) are spread over the
+// waves; each runs the segment's 16 K-blocks in order from +0.
 static constexpr int SK_BN = 64;
 static constexpr int SK_ROWS = 512;  // = KC
 
-__device__ __forceinline__ int sk_phys(int row, int chunk) {  // element offset of a 16-B chunk
+__device__ __forceinline__ int sk_phys(int row, int chunk) {  // W: element offset of a 16-B chunk
   return row * SK_BN + ((chunk ^ (row & 7)) << 3);
 }
+__device__ __forceinline__ int sk_xphys(int row, int chunk) {  // x: rows of 64 chunks
+  return row * SK_ROWS + ((chunk ^ (row & 15)) << 3);
+}
 
-template <bool ALLK>
+template <int MT>  // 16-row sub-tiles of x: 1, 2 or 4
 __global__ __launch_bounds__(512) void gemm_skinny_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, uint16_t* __restrict__ y,
-    float* __restrict__ part, int M, int N, int K, int S) {
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ part,
+    int M, int N, int K) {
   __shared__ __attribute__((aligned(16))) uint16_t wl[SK_ROWS * SK_BN];
+  __shared__ __attribute__((aligned(16))) uint16_t xl[16 * MT * SK_ROWS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -206,85 +81,81 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(
   const int tr_r = (lane & 15) >> 2;
   const int tr_c = lane & 3;
   const int n0 = blockIdx.x * SK_BN;
-  const int seg_begin = ALLK ? 0 : (int)blockIdx.y;
-  const int seg_end = ALLK ? S : (int)blockIdx.y + 1;
+  const int seg = (int)blockIdx.y;
+  const int k0 = seg * SK_ROWS;
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W, (uint32_t)((size_t)K * N * 2));
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
   const uint32_t row_bytes = (uint32_t)N * 2;
 
-  // W slab of one segment: chunk c = tid + 512 i is row c/8, 16-B chunk c%8.
+  // W slab: chunk c = tid + 512 i is row c/8, 16-B chunk c%8.  Rows past K
+  // read as zero.
   u32x4_t wreg[8];
-  auto issue_w = [&](int seg, bool valid) {
-    uint32_t off = (uint32_t)(seg * SK_ROWS + (tid >> 3)) * row_bytes +
-                   (uint32_t)(n0 + (tid & 7) * 8) * 2;
-    if (!valid) off = 0x80000000u;  // past the end: zeros, no memory traffic
+  {
+    uint32_t off = (uint32_t)(k0 + (tid >> 3)) * row_bytes + (uint32_t)(n0 + (tid & 7) * 8) * 2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       wreg[i] = bufld128(wr, off);
-      off = valid ? off + 64 * row_bytes : off;
+      off += 64 * row_bytes;
     }
-  };
-  u32x4_t xc[16];
-  auto issue_x = [&](int seg) {
-    const uint32_t off = (uint32_t)(arow * K + seg * SK_ROWS + g * 8) * 2;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) xc[j] = bufld128(xr, off + j * KB * 2);
-  };
-
-  f32x4_t tot = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  issue_w(seg_begin, true);
-  for (int seg = seg_begin; seg < seg_end; ++seg) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 512 * i;
-      *(u32x4_t*)&wl[sk_phys(c >> 3, c & 7)] = wreg[i];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    if (wave < 4) issue_x(seg);
-    issue_w(seg + 1, seg + 1 < seg_end);
-    if (wave < 4) {
-      const int nkb = min(SK_ROWS, K - seg * SK_ROWS) / KB;
-      const int chunk = 2 * wave + (tr_c >> 1);
-      const int sub = (tr_c & 1) * 4;
-      f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 16; ++kb) {
-        if (kb < nkb) {
-          const int r0 = kb * KB + 8 * g + tr_r;
-          const u32x2_t b0 = lds_read_tr16(&wl[sk_phys(r0, chunk) + sub]);
-          const u32x2_t b1 = lds_read_tr16(&wl[sk_phys(r0 + 4, chunk) + sub]);
-          a = mfma16x16x32(xc[kb], u32x4_t{b0.x, b0.y, b1.x, b1.y}, a);
-        }
-      }
-      const int col = n0 + 16 * wave + arow;
-      if (ALLK) {
-        if (seg == 0)
-          tot = a;
-        else
-          tot = tot + a;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = g * 4 + e;
-          if (m < M) part[((size_t)seg * M + m) * N + col] = a[e];
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   }
-  if (ALLK && wave < 4) {
-    const int col = n0 + 16 * wave + arow;
+  // x slab: chunk c = tid + 512 i is row c/64, 16-B chunk c%64 of the
+  // segment (k past K, within a row, is never multiplied: such K-blocks are
+  // skipped below)
+  u32x4_t xreg[2 * MT];
+#pragma unroll
+  for (int i = 0; i < 2 * MT; ++i) {
+    const int c = tid + 512 * i;
+    const int r = c >> 6, ch = c & 63;
+    xreg[i] = bufld128(xr, r < M ? (uint32_t)(r * K + k0 + ch * 8) * 2 : 0x80000000u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + 512 * i;
+    *(u32x4_t*)&wl[sk_phys(c >> 3, c & 7)] = wreg[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 2 * MT; ++i) {
+    const int c = tid + 512 * i;
+    *(u32x4_t*)&xl[sk_xphys(c >> 6, c & 63)] = xreg[i];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+  // chains of this wave: column group wave%4, sub-tiles (wave/4)*SPW ..
+  constexpr int SPW = MT == 4 ? 2 : 1;        // sub-tiles per wave
+  if (MT == 1 && wave >= 4) return;
+  const int cg = wave & 3;
+  const int sub0 = (wave >> 2) * SPW;
+  const int nkb = min(SK_ROWS, K - k0) / KB;
+  const int chunk = 2 * cg + (tr_c >> 1);
+  const int sub = (tr_c & 1) * 4;
+  f32x4_t a[SPW];
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) a[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 16; ++kb) {
+    if (kb < nkb) {
+      const int r0 = kb * KB + 8 * g + tr_r;
+      const u32x2_t b0 = lds_read_tr16(&wl[sk_phys(r0, chunk) + sub]);
+      const u32x2_t b1 = lds_read_tr16(&wl[sk_phys(r0 + 4, chunk) + sub]);
+      const u32x4_t bf = u32x4_t{b0.x, b0.y, b1.x, b1.y};
+#pragma unroll
+      for (int i = 0; i < SPW; ++i) {
+        const u32x4_t af = *(const u32x4_t*)&xl[sk_xphys((sub0 + i) * 16 + arow, kb * 4 + g)];
+        a[i] = mfma16x16x32(af, bf, a[i]);
+      }
+    }
+  }
+  const int col = n0 + 16 * cg + arow;
+#pragma unroll
+  for (int i = 0; i < SPW; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int m = g * 4 + e;
-      if (m < M) y[(size_t)m * N + col] = (uint16_t)f32_to_bf16_bits(tot[e]);
+      const int m = (sub0 + i) * 16 + g * 4 + e;
+      if (m < M) part[((size_t)seg * M + m) * N + col] = a[i][e];
     }
-  }
 }
 
 // Ordered fold of segment sums: y = bf16(((p0 + p1) + p2) + ...), fp32.
@@ -533,23 +404,19 @@ __global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
 // ---------------------------------------------------------------------------
 static constexpr int BI_KC = 512;  // invariant segment length
 static constexpr int TILE_BM = TL_BM;  // rows per tile-kernel workgroup (8 waves)
-static constexpr int SPLIT_MAX_M = 64;
-static constexpr int SKINNY_MAX_M = 16;
-static constexpr int SKINNY_ALLK_TILES = 256;  // 64-column tiles that fill the chip alone
+static constexpr int SKINNY_MAX_M = 64;
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Which kernels run for (M, N, K).  The bits never depend on it.
 static constexpr int TILE_MIN_TILES = 192;  // fewer tiles than this: split K into slices
 
-enum class GemmPath { Tile, TileSlice, SkinnyAllK, SkinnySeg, Split };
+enum class GemmPath { Tile, TileSlice, Skinny };
 static GemmPath gemm_path(int64_t M, int64_t N) {
-  if (M > SPLIT_MAX_M)
+  if (M > SKINNY_MAX_M)
     return ceil_div(M, TILE_BM) * ceil_div(N, TL_BN) >= TILE_MIN_TILES ? GemmPath::Tile
                                                                          : GemmPath::TileSlice;
-  if (M <= SKINNY_MAX_M) return (N / SK_BN >= SKINNY_ALLK_TILES) ? GemmPath::SkinnyAllK
-                                                                  : GemmPath::SkinnySeg;
-  return GemmPath::Split;
+  return GemmPath::Skinny;
 }
 
 // K slice of the tile kernel: the invariant schedule always uses 512 (one
@@ -567,7 +434,7 @@ static int64_t slice_kc(int64_t M, int64_t N, int64_t K, bool fast, int num_cus)
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool fast, int num_cus) {
   const GemmPath p = gemm_path(M, N);
-  if (p == GemmPath::Tile || p == GemmPath::SkinnyAllK) return 0;
+  if (p == GemmPath::Tile) return 0;
   const int64_t kc = p == GemmPath::TileSlice ? slice_kc(M, N, K, fast, num_cus) : BI_KC;
   return (size_t)ceil_div(K, kc) * (size_t)M * (size_t)N * sizeof(float);
 }
@@ -602,22 +469,19 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
                        0, stream, part, y, (int)M, (int)N, (int)ns);
     return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
   }
-  if (p == GemmPath::SkinnyAllK) {
-    hipLaunchKernelGGL(gemm_skinny_kernel<true>, dim3((unsigned)(N / SK_BN), 1), dim3(512), 0,
-                       stream, x, W, y, (float*)nullptr, (int)M, (int)N, (int)K, (int)S);
-    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
-  }
   if (S > 65535) return BI_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < (size_t)S * (size_t)M * (size_t)N * sizeof(float)) return BI_ERR_WORKSPACE;
   float* part = (float*)ws;
-  if (p == GemmPath::SkinnySeg) {
-    hipLaunchKernelGGL(gemm_skinny_kernel<false>, dim3((unsigned)(N / SK_BN), (unsigned)S),
-                       dim3(512), 0, stream, x, W, y, part, (int)M, (int)N, (int)K, (int)S);
-  } else {
-    dim3 grid((unsigned)(N / SPLIT_BN), (unsigned)S, (unsigned)ceil_div(M, SPLIT_BM));
-    hipLaunchKernelGGL(gemm_split_kernel<4>, grid, dim3(256), 0, stream, x, W, part, (int)M,
-                       (int)N, (int)K, BI_KC);
-  }
+  const dim3 grid((unsigned)(N / SK_BN), (unsigned)S);
+  if (M <= 16)
+    hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(512), 0, stream, x, W, part, (int)M,
+                       (int)N, (int)K);
+  else if (M <= 32)
+    hipLaunchKernelGGL(gemm_skinny_kernel<2>, grid, dim3(512), 0, stream, x, W, part, (int)M,
+                       (int)N, (int)K);
+  else
+    hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(512), 0, stream, x, W, part, (int)M,
+                       (int)N, (int)K);
   if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
   hipLaunchKernelGGL(gemm_fold_kernel, dim3((unsigned)ceil_div(N, 256), (unsigned)M), dim3(64),
                      0, stream, part, y, (int)M, (int)N, (int)S);

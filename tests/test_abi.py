@@ -57,16 +57,16 @@ def test_gemm_argument_checks(lib):
     assert lib.bi_gemm(P(ok), P(ok), P(ok), 1, 48, 32, None, 0, None) == -3   # N % 64
     assert lib.bi_gemm(P(ok + 2), P(ok), P(ok), 1, 64, 32, None, 0, None) == -3  # alignment
     assert lib.bi_gemm(P(ok), P(ok), P(ok), 1 << 20, 1 << 12, 1 << 12, None, 0, None) == -2
-    # 16 < M <= 64 sends segment sums through the workspace
+    # M <= 64 sends segment sums through the workspace
     need = lib.bi_gemm_workspace_bytes(32, 4096, 4096)
     assert need == 8 * 32 * 4096 * 4
     assert lib.bi_gemm(P(ok), P(ok), P(ok), 32, 4096, 4096, P(ok), need - 16, None) == -4
     assert lib.bi_gemm(P(ok), P(ok), P(ok), 32, 4096, 4096, None, 0, None) == -4
-    # decode-sized M: segment sums go through the workspace unless the
-    # 64-column tiles alone fill the chip (N >= 16384); large M folds in registers
+    # decode-sized M: segment sums always go through the workspace; large M
+    # folds in registers
     assert lib.bi_gemm_workspace_bytes(1, 4096, 4096) == 8 * 1 * 4096 * 4
     assert lib.bi_gemm_workspace_bytes(16, 4096, 14336) == 28 * 16 * 4096 * 4
-    assert lib.bi_gemm_workspace_bytes(16, 28672, 4096) == 0
+    assert lib.bi_gemm_workspace_bytes(16, 28672, 4096) == 8 * 16 * 28672 * 4
     assert lib.bi_gemm_workspace_bytes(2048, 4096, 4096) == 0
 
 
