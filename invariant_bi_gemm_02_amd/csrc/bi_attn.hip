@@ -10,7 +10,7 @@
 //   chunk c = tokens [256c, 256c + 256) of the request, one workgroup per
 //   (chunk, kv head, request); inside it, tiles of 64 tokens in order with an
 //   online softmax per q head:
-//     s_t   = (sum_d q_d k_td, dims in order, pairs fused by v_dot2_f32_bf16) * scale
+//     s_t   = (sum_d q_d k_td on the matrix cores, 32-dim blocks in order) * scale
 //     m'    = max(m, max_t s_t);  alpha = exp(m - m') (0 while m = -inf)
 //     l     = l * alpha, then l = l + p_t in token order, p_t = exp(s_t - m')
 //     acc_d = acc_d * alpha, then acc_d = fma(p_t, v_td, acc_d) in token order
@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t ks[ATILE * AKLD];
   __shared__ __attribute__((aligned(16))) uint16_t vs[ATILE * AD];
   __shared__ __attribute__((aligned(16))) float ps[G][ATILE];
+  __shared__ int pgs[ACH / APS];  // page ids of the chunk's tokens
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -72,9 +73,13 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
   const int t_end = min(L, t_begin + C);
   const int32_t* bt = block_table + (size_t)b * max_blocks;
 
-  // q of this kv head's G query heads (bf16, as stored).
+  // q of this kv head's G query heads (bf16, as stored), and the page of
+  // every 16 tokens of the chunk (read once, so that the tile loads below
+  // do not wait on block-table reads)
   for (int i = tid; i < G * AD; i += 256)
     qs[i / AD][i % AD] = q[((size_t)b * Hq + hk * G) * AD + i];
+  if (tid < (t_end - t_begin + APS - 1) / APS) pgs[tid] = bt[t_begin / APS + tid];
+  __syncthreads();
 
   // K/V tile loader: 64 tokens x 16 chunks of 16 B for each of K and V;
   // chunk ci = tid + 256 i: token ci/16, dims 8*(ci%16)..+7.
@@ -89,7 +94,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
       vr[i] = u32x4_t{0u, 0u, 0u, 0u};
       if (tt < nt) {
         const int t = t0 + tt;
-        const long long page = bt[t / APS];
+        const long long page = pgs[(t - t_begin) / APS];
         if (page >= 0 && page < num_pages) {
           const size_t kofs = (((size_t)page * 2 + 0) * Hkv + hk) * (APS * AD) + (t % APS) * AD + dc * 8;
           const size_t vofs = kofs + (size_t)Hkv * APS * AD;
@@ -120,35 +125,45 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
     acc1[j] = 0.0f;
   }
 
+  // q of the group as the B operand of the score products: lane l holds
+  // head l%16 (zero past G), dims 32 kb + 8 (l/16) .. +7
+  u32x4_t bq[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+    bq[kb] = (lane & 15) < G ? *(const u32x4_t*)&qs[lane & 15][kb * 32 + (lane >> 4) * 8]
+                             : u32x4_t{0u, 0u, 0u, 0u};
+
   int nt = min(ATILE, t_end - t_begin);
   load_tile(t_begin, nt);
   for (int t0 = t_begin; t0 < t_end; t0 += ATILE) {
     nt = min(ATILE, t_end - t0);
-    __syncthreads();  // previous tile fully consumed (and q staged)
+    __syncthreads();  // previous tile fully consumed
     store_tile();
     __syncthreads();
     const int t1 = t0 + ATILE;
     if (t1 < t_end) load_tile(t1, min(ATILE, t_end - t1));
 
+    // scores on the matrix cores: wave w takes tokens 16w..16w+15 of the
+    // tile for every head of the group, S^T = K Q^T, 32-dim blocks in order
+    {
+      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* krow = ks + (16 * wave + (lane & 15)) * AKLD + (lane >> 4) * 8;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        sc = mfma16x16x32(*(const u32x4_t*)(krow + kb * 32), bq[kb], sc);
+      if ((lane & 15) < G) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ps[lane & 15][16 * wave + (lane >> 4) * 4 + e] = sc[e] * scale;
+      }
+    }
+    __syncthreads();
+
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       const int hh = wave + 4 * j;
       if (hh < G) {
-        // scores: lane = token
-        float s = -INFINITY;
-        if (lane < nt) {
-          // q.k in dimension order, two dimensions per v_dot2_f32_bf16
-          float dot = 0.0f;
-          const uint16_t* krow = ks + lane * AKLD;
-#pragma unroll 4
-          for (int d0 = 0; d0 < AD; d0 += 8) {
-            const u32x4_t k8 = *(const u32x4_t*)(krow + d0);
-            const u32x4_t q8 = *(const u32x4_t*)&qs[hh][d0];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) dot = dot2_bf16(q8[w], k8[w], dot);
-          }
-          s = dot * scale;
-        }
+        // lane = token
+        const float s = lane < nt ? ps[hh][lane] : -INFINITY;
         float mt = s;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));

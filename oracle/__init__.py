@@ -16,7 +16,8 @@ schedule oracle.  Parity status per function:
                      unpinned at that level (covered by the tolerance).
 * ``rmsnorm``        pinned (fp64 bound, zero and +-1 rows, row independence).
 * ``paged_decode_attn`` pinned (fp64 bound, one-token, constant-V and q=0
-                     cases, page-layout invariance); the last bits of exp are
+                     cases, page-layout invariance); the last bits of exp and
+                     the association inside each 32-dim block of q.k are
                      unpinned (covered by the tolerance).
 """
 from __future__ import annotations

@@ -334,9 +334,9 @@ int or_rmsnorm_exact(const uint16_t *x, const uint16_t *g, double *y,
  *     Lsum = fma(l_c, w_c, Lsum) and O_d = fma(acc_c,d, w_c, O_d), c = 0..,
  *     out_d = bf16(O_d / Lsum).
  * Parity: the exponential (host expf vs the device's own exp) and the
- * grouping inside the q.k dot (the device fuses dimension pairs with one
- * dot-product instruction) are unpinned at the last-bit level and covered by
- * the tolerance; everything else follows the same steps.  Pinned by fp64
+ * grouping inside the q.k dot (the device sums 32-dimension blocks on the
+ * matrix cores, the blocks in order) are unpinned at the last-bit level and
+ * covered by the tolerance; everything else follows the same steps.  Pinned by fp64
  * brute force, the one-token case (out = v_0 exactly), constant V, q = 0,
  * and page-layout invariance.
  */
