@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
 // grid = (num_q_heads, batch), block = 128 (one lane per dim).
 // The chunk maxima and weights are computed by all lanes in parallel (the
 // maximum does not depend on order); the two sums then run in chunk order,
-// with the partials of 16 chunks fetched before each stretch of the chain.
+// with the partials of 32 chunks fetched before each stretch of the chain.
 static constexpr int ACOMB_MAXC = 1024;  // chunks per request the combine handles
 
 __global__ __launch_bounds__(128) void attn_combine_kernel(
@@ -269,19 +269,28 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(
   float ls = 0.0f, acc = 0.0f;
   const float* pd = pp + 4 + d;
   int cc = 0;
-  for (; cc + 16 <= nc; cc += 16) {
-    float v[16];
+  for (; cc + 32 <= nc; cc += 32) {
+    float v[32];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = pd[(size_t)(cc + u) * APART];
+    for (int u = 0; u < 32; ++u) v[u] = pd[(size_t)(cc + u) * APART];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < 32; ++u) {
       ls = __fmaf_rn(lsh[cc + u], wsh[cc + u], ls);
       acc = __fmaf_rn(v[u], wsh[cc + u], acc);
     }
   }
-  for (; cc < nc; ++cc) {
-    ls = __fmaf_rn(lsh[cc], wsh[cc], ls);
-    acc = __fmaf_rn(pd[(size_t)cc * APART], wsh[cc], acc);
+  if (cc < nc) {
+    // the last stretch: its loads issued together as well (zeros past nc)
+    float v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v[u] = cc + u < nc ? pd[(size_t)(cc + u) * APART] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      if (cc + u < nc) {
+        ls = __fmaf_rn(lsh[cc + u], wsh[cc + u], ls);
+        acc = __fmaf_rn(v[u], wsh[cc + u], acc);
+      }
+    }
   }
   o[d] = (uint16_t)f32_to_bf16_bits(acc / ls);  // IEEE division
 }
