@@ -80,6 +80,27 @@ def test_config4_batch_layout_and_grid_invariance(gpu):
         check_close_bf16(full[b:b + 1], want, what=f"request {b} L={cl[b]}")
 
 
+def test_config4_b64_invariance_and_sampled_oracle(gpu):
+    """The largest batch of the workload: B = 64, context lengths uniform in
+    [512, 32768], shuffled pages.  Requests alone and in a permuted batch are
+    bitwise equal to the batch run; 16 sampled requests agree with the
+    oracle."""
+    B = 64
+    ctx = synth.ctx_lens_uniform(B, seed=41)
+    q, kv, bt, cl = synth.attn_inputs(ctx, seed=41)
+    qb, kvb = synth.to_bits(q), synth.to_bits(kv)
+    kvd = synth.from_bits(kvb, DEV)
+    full = run(gpu, qb, kvd, bt, cl)
+    for b in (0, 17, 40, B - 1):
+        alone = run(gpu, qb[b:b + 1], kvd, bt[b:b + 1], cl[b:b + 1])
+        np.testing.assert_array_equal(alone[0], full[b])
+    perm = np.random.default_rng(1).permutation(B)
+    np.testing.assert_array_equal(run(gpu, qb[perm], kvd, bt[perm], cl[perm]), full[perm])
+    for b in range(0, B, 4):
+        want = oracle.paged_decode_attn(qb[b:b + 1], kvb, bt[b:b + 1], cl[b:b + 1], HKV, PS)
+        check_close_bf16(full[b:b + 1], want, what=f"request {b} L={cl[b]}")
+
+
 @pytest.mark.parametrize("B", [1, 4, 64])
 def test_fast_twin_parity(gpu, B):
     ctx = synth.ctx_lens_uniform(B, seed=20 + B, lo=512, hi=8192)

@@ -1,0 +1,115 @@
+"""Output bits do not depend on how much of the GPU a call gets: the same
+calls on streams restricted to 32 or 64 CUs, and while another stream keeps
+the memory system busy, give bitwise the same results as on a free device.
+The batch-invariant entry points never read the CU count, so no schedule can
+change with it; these tests check that nothing else does either (the
+Vosti abstract's independence of engine state, the Determinism article's
+section 6 on runtime variation)."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from invariant_bi_gemm_02_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+PS, HKV = 16, 8
+
+
+def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.fixture(scope="module")
+def masked_streams(gpu):
+    """Streams whose kernels may use only the first 32 / 64 CUs."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (n_cu + 31) // 32
+    made = []
+    for n in (32, 64):
+        mask = (ctypes.c_uint32 * words)()
+        for i in range(min(n, n_cu)):
+            mask[i // 32] |= 1 << (i % 32)
+        handle = ctypes.c_void_p()
+        err = hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), ctypes.c_uint32(words), mask)
+        assert err == 0, f"hipExtStreamCreateWithCUMask failed: {err}"
+        made.append((n, handle))
+    yield [(n, torch.cuda.ExternalStream(h.value)) for n, h in made]
+    torch.cuda.synchronize()
+    for _, h in made:
+        hip.hipStreamDestroy(h)
+
+
+def on_stream(stream, fn, *args):
+    with torch.cuda.stream(stream):
+        out = fn(*args)
+    stream.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("M", [1, 16, 40, 300, 2048])
+def test_gemm_bits_under_cu_masks(gpu, masked_streams, M):
+    x, w = synth.gemm_inputs(M, 4096, 4096, seed=31 + M, device=DEV)
+    ref = gpu.gemm(x, w)
+    torch.cuda.synchronize()
+    for n, s in masked_streams:
+        assert same_bits(on_stream(s, gpu.gemm, x, w), ref), f"M={M} on {n} CUs"
+
+
+def test_rmsnorm_bits_under_cu_masks(gpu, masked_streams):
+    x, g = synth.rmsnorm_inputs(512, 4096, seed=32, device=DEV)
+    ref = gpu.rmsnorm(x, g)
+    torch.cuda.synchronize()
+    for n, s in masked_streams:
+        assert same_bits(on_stream(s, gpu.rmsnorm, x, g), ref), f"on {n} CUs"
+
+
+def _attn_case(B, seed, hi=32768):
+    ctx = synth.ctx_lens_uniform(B, seed=seed, hi=hi)
+    q, kv, bt, cl = synth.attn_inputs(ctx, seed=seed)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return q.to(DEV), kv.to(DEV), t(bt), t(cl), int(cl.max())
+
+
+def test_attention_bits_under_cu_masks(gpu, masked_streams):
+    q, kv, bt, cl, mc = _attn_case(8, 33)
+    ref = gpu.paged_decode_attn(q, kv, bt, cl, mc)
+    torch.cuda.synchronize()
+    for n, s in masked_streams:
+        got = on_stream(s, gpu.paged_decode_attn, q, kv, bt, cl, mc)
+        assert same_bits(got, ref), f"on {n} CUs"
+
+
+def test_bits_under_concurrent_memory_load(gpu):
+    """A second stream copies 512 MB buffers back and forth while the calls
+    run; the results match the ones taken on an idle device."""
+    x, w = synth.gemm_inputs(2048, 4096, 4096, seed=34, device=DEV)
+    x1 = x[:1].contiguous()
+    q, kv, bt, cl, mc = _attn_case(8, 35)
+    ref_big, ref_one = gpu.gemm(x, w), gpu.gemm(x1, w)
+    ref_att = gpu.paged_decode_attn(q, kv, bt, cl, mc)
+    torch.cuda.synchronize()
+    a = torch.empty(256 << 20, dtype=torch.int16, device=DEV)
+    b = torch.empty_like(a)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for _ in range(6):
+            b.copy_(a)
+            a.copy_(b)
+    for _ in range(3):
+        assert same_bits(gpu.gemm(x, w), ref_big)
+        assert same_bits(gpu.gemm(x1, w), ref_one)
+        assert same_bits(gpu.paged_decode_attn(q, kv, bt, cl, mc), ref_att)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [1, 2048])
+def test_gemm_hundred_repeats(gpu, M):
+    x, w = synth.gemm_inputs(M, 4096, 6144, seed=36, device=DEV)
+    ref = gpu.gemm(x, w)
+    outs = [gpu.gemm(x, w) for _ in range(100)]
+    torch.cuda.synchronize()
+    assert all(same_bits(o, ref) for o in outs)
