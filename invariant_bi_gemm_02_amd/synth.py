@@ -146,3 +146,76 @@ def relayout_kv(kv_bits: np.ndarray, bt: np.ndarray, ctx_lens, page_size: int, s
             kv2[dst, :, :, :valid, :] = kv_bits[src, :, :, :valid, :]
         off += int(n)
     return kv2, bt2
+
+
+# ---------------------------------------------------------------------------
+# Decoder (Llama-3-8B-shaped, random init) and LLM-42-style verify batches
+# ---------------------------------------------------------------------------
+
+class DecoderConfig:
+    """Sizes of a Llama-style decoder (no arithmetic here)."""
+
+    def __init__(self, layers=32, hidden=4096, q_heads=32, kv_heads=8, ffn=14336,
+                 vocab=128256, theta=5e5, eps=1e-5, head_dim=128, page_size=16):
+        self.layers, self.hidden, self.q_heads, self.kv_heads = layers, hidden, q_heads, kv_heads
+        self.ffn, self.vocab, self.theta, self.eps = ffn, vocab, theta, eps
+        self.head_dim, self.page_size = head_dim, page_size
+
+    @property
+    def qkv_width(self) -> int:
+        return (self.q_heads + 2 * self.kv_heads) * self.head_dim
+
+
+LLAMA3_8B = DecoderConfig()
+# A small configuration with the same head shape, for oracle comparisons.
+TINY = DecoderConfig(layers=2, hidden=512, q_heads=4, kv_heads=2, ffn=1024, vocab=1024)
+
+
+def decoder_weights(cfg: DecoderConfig, seed: int, device="cpu") -> dict:
+    """Random-init bf16 weights: matrices N(0, 0.02^2) laid out [in, out]
+    (y = x W), gains N(1, 0.1^2), embedding N(0, 1)."""
+    w = {"embed": bf16_normal((cfg.vocab, cfg.hidden), seed * 100 + 1, device=device)}
+    for l in range(cfg.layers):
+        b = seed * 100 + 10 + 8 * l
+        w[f"{l}.attn_norm"] = bf16_normal((cfg.hidden,), b, mean=1.0, std=0.1, device=device)
+        w[f"{l}.wqkv"] = bf16_normal((cfg.hidden, cfg.qkv_width), b + 1, std=0.02, device=device)
+        w[f"{l}.wo"] = bf16_normal((cfg.q_heads * cfg.head_dim, cfg.hidden), b + 2, std=0.02,
+                                   device=device)
+        w[f"{l}.ffn_norm"] = bf16_normal((cfg.hidden,), b + 3, mean=1.0, std=0.1, device=device)
+        w[f"{l}.wgu"] = bf16_normal((cfg.hidden, 2 * cfg.ffn), b + 4, std=0.02, device=device)
+        w[f"{l}.wdown"] = bf16_normal((cfg.ffn, cfg.hidden), b + 5, std=0.02, device=device)
+    w["final_norm"] = bf16_normal((cfg.hidden,), seed * 100 + 2, mean=1.0, std=0.1,
+                                  device=device)
+    w["lm_head"] = bf16_normal((cfg.hidden, cfg.vocab), seed * 100 + 3, std=0.02, device=device)
+    return w
+
+
+class Requests:
+    """A set of requests sharing one page pool per layer: prompt tokens, and
+    for each request a block table row with room for max_len tokens.  Pages
+    are handed out from a shuffled pool."""
+
+    def __init__(self, prompt_lens, max_len: int, vocab: int, page_size: int, seed: int):
+        rng = np.random.default_rng(seed)
+        self.prompt_lens = [int(x) for x in prompt_lens]
+        self.max_blocks = -(-max_len // page_size)
+        n = len(self.prompt_lens)
+        self.num_pages = n * self.max_blocks
+        perm = rng.permutation(self.num_pages).astype(np.int32)
+        self.block_table = perm.reshape(n, self.max_blocks)
+        self.prompts = [rng.integers(0, vocab, size=L).astype(np.int32) for L in self.prompt_lens]
+
+    def rows(self, req_ids, positions, tokens):
+        """Per-row arrays for a forward over (request, position, token) rows."""
+        req_ids = np.asarray(req_ids, dtype=np.int64)
+        return (np.asarray(tokens, dtype=np.int32), np.asarray(positions, dtype=np.int32),
+                np.ascontiguousarray(self.block_table[req_ids]))
+
+
+def verify_groups(n_requests: int, total: int, seed: int):
+    """LLM-42-style grouped verification: split `total` window tokens over
+    the requests (each gets at least one), in a shuffled row order."""
+    rng = np.random.default_rng(seed)
+    cuts = np.sort(rng.choice(np.arange(1, total), size=n_requests - 1, replace=False))
+    sizes = np.diff(np.concatenate([[0], cuts, [total]]))
+    return [int(s) for s in sizes]

@@ -30,7 +30,7 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "bi_oracle.c")
+_SRCS = [os.path.join(_HERE, "bi_oracle.c"), os.path.join(_HERE, "bi_oracle_layer.c")]
 _LIB = os.path.join(_HERE, "libbi_oracle.so")
 _CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
            "-shared", "-Wall", "-Wextra"]
@@ -40,11 +40,12 @@ _lib = None
 
 
 def build(force: bool = False) -> str:
-    """Compile bi_oracle.c into oracle/libbi_oracle.so with gcc."""
+    """Compile the oracle's C sources into oracle/libbi_oracle.so with gcc."""
+    deps = _SRCS + [os.path.join(_HERE, "bi_oracle.h")]
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
-            os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "bi_oracle.h"))):
+            os.path.getmtime(f) for f in deps):
         tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, *_SRCS, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -71,9 +72,14 @@ def _load():
                                                  ctypes.c_float]
             lib.or_paged_decode_attn_exact.argtypes = [p, p, p, p, p, i64, ci, ci, ci, ci,
                                                        i64, ctypes.c_double]
+            lib.or_rope_table.argtypes = [ctypes.c_double, ci, i64, p, p]
+            lib.or_rope.argtypes = [p, p, p, i64, ci, ci, i64, p, p, i64]
+            lib.or_silu_mul.argtypes = [p, p, i64, i64]
+            lib.or_add.argtypes = [p, p, p, i64]
             for f in ("or_gemm", "or_gemm_exact", "or_gemm_absdot", "or_rmsnorm",
                       "or_rmsnorm_exact", "or_paged_decode_attn",
-                      "or_paged_decode_attn_exact"):
+                      "or_paged_decode_attn_exact", "or_rope_table", "or_rope",
+                      "or_silu_mul", "or_add"):
                 getattr(lib, f).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -207,3 +213,51 @@ def paged_decode_attn_exact(q, kv, block_table, ctx_lens, num_kv_heads: int = 8,
                                               B, Hq, num_kv_heads, D, page_size, bt.shape[1],
                                               scale), "paged_decode_attn_exact")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Element-wise steps of the decoder layer (bi_oracle_layer.c)
+# ---------------------------------------------------------------------------
+
+def rope_table(theta: float, D: int, max_pos: int):
+    """cos, sin as float32 [max_pos, D/2]: angle p * theta^(-2i/D) in double,
+    each rounded once to fp32."""
+    c = np.empty((max_pos, D // 2), dtype=np.float32)
+    s = np.empty((max_pos, D // 2), dtype=np.float32)
+    _check(_load().or_rope_table(ctypes.c_double(theta), D, max_pos, _ptr(c), _ptr(s)),
+           "rope_table")
+    return c, s
+
+
+def rope(x, pos, heads: int, D: int, cos_t, sin_t):
+    """Rotate-half RoPE of the first heads*D values of every row of x (bf16
+    bits [M, >= heads*D]); returns [M, heads, D] bits."""
+    x = _u16(x)
+    M = x.shape[0]
+    stride = int(np.prod(x.shape[1:])) if x.ndim > 1 else 0
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    c = np.ascontiguousarray(cos_t, dtype=np.float32)
+    s = np.ascontiguousarray(sin_t, dtype=np.float32)
+    y = np.empty((M, heads, D), dtype=np.uint16)
+    _check(_load().or_rope(_ptr(x), _ptr(y), _ptr(pos), M, heads, D, stride, _ptr(c), _ptr(s),
+                           c.shape[0]), "rope")
+    return y
+
+
+def silu_mul(gu):
+    """bf16(silu(gate) * up) for gu = [gate | up] bf16 bits [M, 2F]."""
+    gu = _u16(gu)
+    M, F2 = gu.shape
+    y = np.empty((M, F2 // 2), dtype=np.uint16)
+    _check(_load().or_silu_mul(_ptr(gu), _ptr(y), M, F2 // 2), "silu_mul")
+    return y
+
+
+def add(a, b):
+    """bf16(a + b) element-wise, one fp32 addition."""
+    a, b = _u16(a), _u16(b)
+    if a.shape != b.shape:
+        raise ValueError("shapes differ")
+    y = np.empty_like(a)
+    _check(_load().or_add(_ptr(a), _ptr(b), _ptr(y), a.size), "add")
+    return y

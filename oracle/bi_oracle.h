@@ -33,4 +33,12 @@ int or_paged_decode_attn_exact(const uint16_t *q, const uint16_t *kv,
                                const int32_t *ctx_lens, double *out, int64_t B,
                                int Hq, int Hkv, int D, int PS,
                                int64_t max_blocks, double scale);
+
+/* bi_oracle_layer.c: element-wise steps of the decoder layer */
+int or_rope_table(double theta, int D, int64_t max_pos, float *cos_t, float *sin_t);
+int or_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, int64_t M, int heads,
+            int D, int64_t x_stride, const float *cos_t, const float *sin_t,
+            int64_t max_pos);
+int or_silu_mul(const uint16_t *gu, uint16_t *y, int64_t M, int64_t F);
+int or_add(const uint16_t *a, const uint16_t *b, uint16_t *y, int64_t n);
 #endif
