@@ -183,6 +183,74 @@ int bi_paged_decode_attn_fast(const bi_bf16 *q, const bi_bf16 *kv_pages,
                               const bi_attn_desc *d, void *ws, size_t ws_bytes,
                               void *stream);
 
+/* ------------------------------------------------------------------------
+ * Element-wise steps of a Llama-style decoder layer built around the three
+ * calls above.  [LLM-42] problem statement: a token's logits must come out
+ * the same whether it is verified alone or grouped with other requests, so
+ * every step of the forward has to be row-independent; each of these is (one
+ * fixed sequence of fp32 operations and a single round-to-nearest-even bf16
+ * rounding per output element).  The pages name the steps only; the formulas
+ * are the standard Llama ones.  All pointers are device pointers except where
+ * a call says host; nothing is allocated; errors come back as BI_ERR_* with
+ * nothing enqueued.  Device-side ids and positions are not range-checked by
+ * the host: out-of-range ones are handled as each call states.
+ * ---------------------------------------------------------------------- */
+
+/* Token embedding: out[m,:] = table[tokens[m],:].  tokens: [M] int32 (ids
+ * outside [0, V) give a zero row).  table: [V,H] bf16.  out: [M,H] bf16.
+ * Requirements: M, V, H >= 1; H % 8 == 0; 16-byte aligned table and out. */
+int bi_embed(const int32_t *tokens, const bi_bf16 *table, bi_bf16 *out,
+             int64_t M, int64_t V, int64_t H, void *stream);
+
+/* Rotary position table, computed on the HOST into host arrays cos_t and
+ * sin_t of max_pos * head_dim/2 floats each: angle p * theta^(-2i/head_dim)
+ * in double precision for pair i, then cos and sin each rounded once to
+ * fp32.  Copy both to the device for bi_rope.  Requirements: theta > 0,
+ * head_dim even and >= 2, max_pos >= 1, non-null arrays. */
+int bi_rope_table(double theta, int32_t head_dim, int64_t max_pos,
+                  float *cos_t, float *sin_t);
+
+/* Rotary position embedding (rotate-half pairs i, i + D/2, D = 128) of the
+ * first heads*128 values of every row of x:
+ *   out[m,h,i]     = bf16(x_i c - x_{i+64} s),
+ *   out[m,h,i+64]  = bf16(x_{i+64} c + x_i s),  c, s of position pos[m],
+ * each product rounded to fp32 before the sum.  x: rows of x_row_stride
+ * elements (so a slice of a fused q|k|v row can be read in place).  out:
+ * [M, heads, 128] bf16.  pos: [M] int32; positions outside [0, max_pos)
+ * give zeros.  cos_t, sin_t: device copies of the bi_rope_table arrays.
+ * Requirements: M, heads >= 1; head_dim == 128; x_row_stride >= heads*128. */
+int bi_rope(const bi_bf16 *x, int64_t x_row_stride, bi_bf16 *out,
+            const int32_t *pos, const float *cos_t, const float *sin_t,
+            int64_t M, int32_t heads, int32_t head_dim, int64_t max_pos,
+            void *stream);
+
+/* KV-cache append: row m's key and value head vectors (num_kv_heads of 128
+ * each, rows k_row_stride / v_row_stride elements apart) are copied to slot
+ * pos[m] % page_size of page block_table[m][pos[m] / page_size] of the
+ * [num_pages][2][num_kv_heads][page_size][128] cache that
+ * bi_paged_decode_attn reads.  block_table: [M, max_blocks] int32, one row
+ * per appended row.  Rows whose page is negative or >= num_pages are
+ * skipped.  Two rows must not name the same slot (they would race).
+ * Requirements: head_dim == 128; page_size == 16; strides multiples of 8;
+ * 16-byte aligned k, v and kv_pages. */
+int bi_kv_append(const bi_bf16 *k, int64_t k_row_stride, const bi_bf16 *v,
+                 int64_t v_row_stride, bi_bf16 *kv_pages,
+                 const int32_t *block_table, const int32_t *pos, int64_t M,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                 int32_t max_blocks, int64_t num_pages, void *stream);
+
+/* SiLU-gated product of an up projection laid out [gate | up]:
+ *   out[m,f] = bf16( (g / (1 + exp(-g))) * u ),  g = gu[m,f], u = gu[m,F+f],
+ * in fp32 (device exp, IEEE division).  gu: [M, 2F] bf16; out: [M, F] bf16.
+ * Requirements: M, F >= 1; F % 8 == 0; 16-byte aligned gu and out. */
+int bi_silu_mul(const bi_bf16 *gu, bi_bf16 *out, int64_t M, int64_t F,
+                void *stream);
+
+/* Residual add: out = bf16(a + b), one fp32 addition per element.  n values;
+ * out may alias a or b.  Requirements: n >= 1; n % 8 == 0; 16-byte aligned. */
+int bi_add(const bi_bf16 *a, const bi_bf16 *b, bi_bf16 *out, int64_t n,
+           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

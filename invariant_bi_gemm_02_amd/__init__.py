@@ -20,4 +20,10 @@ from ._lib import (  # noqa: F401
     attn_workspace_bytes,
     attn_fast_workspace_bytes,
     Workspace,
+    embed,
+    rope_table,
+    rope,
+    kv_append,
+    silu_mul,
+    add,
 )

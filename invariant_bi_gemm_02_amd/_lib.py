@@ -36,7 +36,8 @@ class AttnDesc(ctypes.Structure):
 EXPORTS = ("bi_version", "bi_status_string", "bi_gemm_workspace_bytes", "bi_gemm",
            "bi_gemm_fast_workspace_bytes", "bi_gemm_fast", "bi_rmsnorm", "bi_rmsnorm_fast",
            "bi_attn_workspace_bytes", "bi_paged_decode_attn", "bi_attn_fast_workspace_bytes",
-           "bi_paged_decode_attn_fast")
+           "bi_paged_decode_attn_fast", "bi_embed", "bi_rope_table", "bi_rope", "bi_kv_append",
+           "bi_silu_mul", "bi_add")
 
 _lock = threading.Lock()
 _lib = None
@@ -74,6 +75,18 @@ def load(path: str | None = None):
         for f in ("bi_paged_decode_attn", "bi_paged_decode_attn_fast"):
             getattr(lib, f).restype = ctypes.c_int
             getattr(lib, f).argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(AttnDesc), vp, sz, vp]
+        i32 = ctypes.c_int32
+        sigs = {
+            "bi_embed": [vp, vp, vp, i64, i64, i64, vp],
+            "bi_rope_table": [ctypes.c_double, i32, i64, vp, vp],
+            "bi_rope": [vp, i64, vp, vp, vp, vp, i64, i32, i32, i64, vp],
+            "bi_kv_append": [vp, i64, vp, i64, vp, vp, vp, i64, i32, i32, i32, i32, i64, vp],
+            "bi_silu_mul": [vp, vp, i64, i64, vp],
+            "bi_add": [vp, vp, vp, i64, vp],
+        }
+        for f, a in sigs.items():
+            getattr(lib, f).restype = ctypes.c_int
+            getattr(lib, f).argtypes = a
         _lib = lib
         return lib
 
@@ -256,3 +269,99 @@ def paged_decode_attn_fast(q, kv_pages, block_table, ctx_lens, max_ctx_len=None,
     """Paged decode attention with batch-dependent splits (not batch-invariant)."""
     return _attn("bi_paged_decode_attn_fast", "bi_attn_fast_workspace_bytes", q, kv_pages,
                  block_table, ctx_lens, max_ctx_len, scale, out, ws)
+
+
+# ---------------------------------------------------------------------------
+# Decoder-layer element-wise steps
+# ---------------------------------------------------------------------------
+
+def _check_i32(t: torch.Tensor, name: str):
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 device tensor")
+
+
+def embed(tokens, table, out=None):
+    """out[m] = table[tokens[m]] (ids outside the table give zero rows)."""
+    lib = load()
+    _check_i32(tokens, "tokens")
+    _check_bf16(table, "table", 2)
+    M, (V, H) = tokens.shape[0], table.shape
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=table.device)
+    _raise(lib.bi_embed(tokens.data_ptr(), table.data_ptr(), out.data_ptr(), M, V, H,
+                        _stream(table.device)), "bi_embed")
+    return out
+
+
+def rope_table(theta: float, head_dim: int, max_pos: int, device="cuda"):
+    """(cos, sin) float32 device tensors [max_pos, head_dim/2] built by the
+    library on the host (angle in double, one rounding to fp32 each)."""
+    lib = load()
+    c = torch.empty((max_pos, head_dim // 2), dtype=torch.float32)
+    s = torch.empty_like(c)
+    _raise(lib.bi_rope_table(ctypes.c_double(theta), head_dim, max_pos, c.data_ptr(),
+                             s.data_ptr()), "bi_rope_table")
+    return c.to(device), s.to(device)
+
+
+def rope(x, heads: int, pos, cos_t, sin_t, out=None):
+    """RoPE of the first heads*128 values of each row of x ([M, >= heads*128]
+    bf16, rows may be strided, e.g. a slice of a fused q|k|v row)."""
+    lib = load()
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise TypeError("x must be a 2-D bf16 device tensor with unit column stride")
+    _check_i32(pos, "pos")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, heads, 128), dtype=torch.bfloat16, device=x.device)
+    for t, n in ((cos_t, "cos"), (sin_t, "sin")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{n} table must be a contiguous float32 device tensor")
+    _raise(lib.bi_rope(x.data_ptr(), x.stride(0), out.data_ptr(), pos.data_ptr(),
+                       cos_t.data_ptr(), sin_t.data_ptr(), M, heads, 128, cos_t.shape[0],
+                       _stream(x.device)), "bi_rope")
+    return out
+
+
+def kv_append(k, v, kv_pages, block_table, pos):
+    """Write k, v ([M, >= Hkv*128] bf16, rows may be strided) into their
+    cache slots (kv_pages [P, 2, Hkv, 16, 128]); block_table is [M, MB]."""
+    lib = load()
+    _check_bf16(kv_pages, "kv_pages", 5)
+    _check_i32(block_table, "block_table")
+    _check_i32(pos, "pos")
+    for t, n in ((k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+            raise TypeError(f"{n} must be a 2-D bf16 device tensor with unit column stride")
+    P, _, Hkv, PS, D = kv_pages.shape
+    _raise(lib.bi_kv_append(k.data_ptr(), k.stride(0), v.data_ptr(), v.stride(0),
+                            kv_pages.data_ptr(), block_table.data_ptr(), pos.data_ptr(),
+                            k.shape[0], Hkv, D, PS, block_table.shape[1], P,
+                            _stream(k.device)), "bi_kv_append")
+
+
+def silu_mul(gu, out=None):
+    """bf16(silu(gate) * up) for gu = [gate | up] of shape [M, 2F]."""
+    lib = load()
+    _check_bf16(gu, "gu", 2)
+    M, F2 = gu.shape
+    if out is None:
+        out = torch.empty((M, F2 // 2), dtype=torch.bfloat16, device=gu.device)
+    _raise(lib.bi_silu_mul(gu.data_ptr(), out.data_ptr(), M, F2 // 2, _stream(gu.device)),
+           "bi_silu_mul")
+    return out
+
+
+def add(a, b, out=None):
+    """bf16(a + b) element-wise (one fp32 addition)."""
+    lib = load()
+    for t, n in ((a, "a"), (b, "b")):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous bf16 device tensor")
+    if a.shape != b.shape:
+        raise ValueError("a and b differ in shape")
+    if out is None:
+        out = torch.empty_like(a)
+    _raise(lib.bi_add(a.data_ptr(), b.data_ptr(), out.data_ptr(), a.numel(), _stream(a.device)),
+           "bi_add")
+    return out

@@ -182,4 +182,67 @@ int bi_paged_decode_attn_fast(const bi_bf16* q, const bi_bf16* kv_pages,
   return attn_entry(q, kv_pages, block_table, ctx_lens, out, d, ws, ws_bytes, stream, true);
 }
 
+int bi_embed(const int32_t* tokens, const bi_bf16* table, bi_bf16* out, int64_t M, int64_t V,
+             int64_t H, void* stream) {
+  if (!tokens || !table || !out) return BI_ERR_NULL;
+  if (M <= 0 || V <= 0 || H <= 0 || M >= kMaxElems || V * H >= ((int64_t)1 << 40) ||
+      M * H >= kMaxElems)
+    return BI_ERR_SHAPE;
+  if (H % 8 != 0 || !aligned16(table) || !aligned16(out) || ((uintptr_t)tokens & 3u))
+    return BI_ERR_UNSUPPORTED;
+  return bi::launch_embed(tokens, table, out, M, V, H, (hipStream_t)stream);
+}
+
+int bi_rope_table(double theta, int32_t head_dim, int64_t max_pos, float* cos_t, float* sin_t) {
+  if (!cos_t || !sin_t) return BI_ERR_NULL;
+  if (!(theta > 0.0) || head_dim < 2 || head_dim % 2 != 0 || max_pos <= 0 ||
+      max_pos * head_dim >= kMaxElems)
+    return BI_ERR_SHAPE;
+  return bi::rope_table_host(theta, head_dim, max_pos, cos_t, sin_t);
+}
+
+int bi_rope(const bi_bf16* x, int64_t x_row_stride, bi_bf16* out, const int32_t* pos,
+            const float* cos_t, const float* sin_t, int64_t M, int32_t heads, int32_t head_dim,
+            int64_t max_pos, void* stream) {
+  if (!x || !out || !pos || !cos_t || !sin_t) return BI_ERR_NULL;
+  if (M <= 0 || heads <= 0 || max_pos <= 0 || M >= kMaxElems || heads > 65535 ||
+      x_row_stride < (int64_t)heads * 128 || M * x_row_stride >= kMaxElems)
+    return BI_ERR_SHAPE;
+  if (head_dim != 128 || ((uintptr_t)x & 1u) || ((uintptr_t)out & 1u) || ((uintptr_t)pos & 3u))
+    return BI_ERR_UNSUPPORTED;
+  return bi::launch_rope(x, x_row_stride, out, pos, cos_t, sin_t, M, heads, max_pos,
+                         (hipStream_t)stream);
+}
+
+int bi_kv_append(const bi_bf16* k, int64_t k_row_stride, const bi_bf16* v, int64_t v_row_stride,
+                 bi_bf16* kv_pages, const int32_t* block_table, const int32_t* pos, int64_t M,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t max_blocks,
+                 int64_t num_pages, void* stream) {
+  if (!k || !v || !kv_pages || !block_table || !pos) return BI_ERR_NULL;
+  if (M <= 0 || num_kv_heads <= 0 || num_kv_heads > 65535 || max_blocks <= 0 ||
+      num_pages <= 0 || M >= kMaxElems || M * (int64_t)max_blocks >= kMaxElems ||
+      k_row_stride < (int64_t)num_kv_heads * 128 || v_row_stride < (int64_t)num_kv_heads * 128)
+    return BI_ERR_SHAPE;
+  if (head_dim != 128 || page_size != 16 || k_row_stride % 8 != 0 || v_row_stride % 8 != 0 ||
+      !aligned16(k) || !aligned16(v) || !aligned16(kv_pages) || ((uintptr_t)block_table & 3u) ||
+      ((uintptr_t)pos & 3u))
+    return BI_ERR_UNSUPPORTED;
+  return bi::launch_kv_append(k, k_row_stride, v, v_row_stride, kv_pages, block_table, pos, M,
+                              num_kv_heads, max_blocks, num_pages, (hipStream_t)stream);
+}
+
+int bi_silu_mul(const bi_bf16* gu, bi_bf16* out, int64_t M, int64_t F, void* stream) {
+  if (!gu || !out) return BI_ERR_NULL;
+  if (M <= 0 || F <= 0 || M > 65535 || M * 2 * F >= kMaxElems) return BI_ERR_SHAPE;
+  if (F % 8 != 0 || !aligned16(gu) || !aligned16(out)) return BI_ERR_UNSUPPORTED;
+  return bi::launch_silu_mul(gu, out, M, F, (hipStream_t)stream);
+}
+
+int bi_add(const bi_bf16* a, const bi_bf16* b, bi_bf16* out, int64_t n, void* stream) {
+  if (!a || !b || !out) return BI_ERR_NULL;
+  if (n <= 0 || n >= kMaxElems) return BI_ERR_SHAPE;
+  if (n % 8 != 0 || !aligned16(a) || !aligned16(b) || !aligned16(out)) return BI_ERR_UNSUPPORTED;
+  return bi::launch_add(a, b, out, n, (hipStream_t)stream);
+}
+
 }  // extern "C"

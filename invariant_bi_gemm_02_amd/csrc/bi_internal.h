@@ -26,6 +26,21 @@ int launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* block_tabl
                 const int32_t* ctx_lens, uint16_t* out, const bi_attn_desc* d, void* ws,
                 size_t ws_bytes, hipStream_t stream, bool fast, int num_cus);
 
+// Decoder-layer element-wise steps (bi_layer.hip)
+int launch_embed(const int32_t* tokens, const uint16_t* table, uint16_t* out, int64_t M,
+                 int64_t V, int64_t H, hipStream_t stream);
+int rope_table_host(double theta, int D, int64_t max_pos, float* cos_t, float* sin_t);
+int launch_rope(const uint16_t* x, int64_t x_stride, uint16_t* out, const int32_t* pos,
+                const float* cos_t, const float* sin_t, int64_t M, int heads, int64_t max_pos,
+                hipStream_t stream);
+int launch_kv_append(const uint16_t* k, int64_t k_stride, const uint16_t* v, int64_t v_stride,
+                     uint16_t* kv, const int32_t* block_table, const int32_t* pos, int64_t M,
+                     int Hkv, int max_blocks, int64_t num_pages, hipStream_t stream);
+int launch_silu_mul(const uint16_t* gu, uint16_t* out, int64_t M, int64_t F,
+                    hipStream_t stream);
+int launch_add(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n,
+               hipStream_t stream);
+
 // Schedule constants reported by bi_version().
 static constexpr int SCHED_GEMM_KB = 32;
 static constexpr int SCHED_GEMM_KC = 512;

@@ -1,0 +1,61 @@
+"""A Llama-style decoder forward assembled from the library's calls.
+
+Orchestration only: every arithmetic step is one of the C-ABI calls (the
+batch-invariant GEMM, RMSNorm and paged decode attention, and the
+element-wise embedding, RoPE, KV append, SiLU product and residual add), run
+on torch's current stream; torch supplies buffers.  Each row of a forward is
+one token of some request at some position, attending to its request's KV
+cache up to and including itself, so a batch may mix any number of requests
+and window lengths -- the LLM-42 digest's grouped verification, where the
+tokens of several requests are checked in one fixed-shape pass.  Since every
+call is row-independent, a row's logits are bit-identical whether it is run
+alone, with the rest of its request, or grouped with other requests.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as bi
+
+
+class Decoder:
+    def __init__(self, cfg, weights: dict, num_pages: int, max_pos: int, device="cuda"):
+        if cfg.head_dim != 128 or cfg.page_size != 16:
+            raise ValueError("the kernels take head_dim 128 and page size 16")
+        self.cfg, self.w, self.device = cfg, weights, device
+        shape = (num_pages, 2, cfg.kv_heads, cfg.page_size, cfg.head_dim)
+        self.kv = [torch.zeros(shape, dtype=torch.bfloat16, device=device)
+                   for _ in range(cfg.layers)]
+        self.cos, self.sin = bi.rope_table(cfg.theta, cfg.head_dim, max_pos, device)
+        self.max_pos = max_pos
+
+    def forward(self, tokens, positions, block_table) -> torch.Tensor:
+        """Logits [M, vocab] (bf16) for rows given as host arrays: tokens [M],
+        positions [M] and block_table [M, max_blocks] (the row's request)."""
+        cfg, w = self.cfg, self.w
+        dev = self.device
+        positions = np.asarray(positions, dtype=np.int32)
+        if positions.min() < 0 or positions.max() >= self.max_pos:
+            raise ValueError("position outside the rope table")
+        tok = torch.from_numpy(np.ascontiguousarray(tokens, dtype=np.int32)).to(dev)
+        pos = torch.from_numpy(positions).to(dev)
+        ctx = torch.from_numpy(positions + 1).to(dev)           # attend up to itself
+        bt = torch.from_numpy(np.ascontiguousarray(block_table, dtype=np.int32)).to(dev)
+        max_ctx = int(positions.max()) + 1
+        M = tok.shape[0]
+        qd, kd = cfg.q_heads * cfg.head_dim, cfg.kv_heads * cfg.head_dim
+
+        h = bi.embed(tok, w["embed"])
+        for l in range(cfg.layers):
+            x = bi.rmsnorm(h, w[f"{l}.attn_norm"], cfg.eps)
+            qkv = bi.gemm(x, w[f"{l}.wqkv"])
+            q = bi.rope(qkv[:, :qd], cfg.q_heads, pos, self.cos, self.sin)
+            k = bi.rope(qkv[:, qd:qd + kd], cfg.kv_heads, pos, self.cos, self.sin)
+            bi.kv_append(k.view(M, kd), qkv[:, qd + kd:], self.kv[l], bt, pos)
+            att = bi.paged_decode_attn(q, self.kv[l], bt, ctx, max_ctx_len=max_ctx)
+            h = bi.add(h, bi.gemm(att.view(M, qd), w[f"{l}.wo"]))
+            x = bi.rmsnorm(h, w[f"{l}.ffn_norm"], cfg.eps)
+            a = bi.silu_mul(bi.gemm(x, w[f"{l}.wgu"]))
+            h = bi.add(h, bi.gemm(a, w[f"{l}.wdown"]))
+        return bi.gemm(bi.rmsnorm(h, w["final_norm"], cfg.eps), w["lm_head"])

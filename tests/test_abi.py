@@ -115,3 +115,37 @@ def test_static_lint_no_float_atomics_or_cu_count_in_invariant_paths():
         assert "__hip_atomic" not in text and "atomicAdd" not in text, fn
         if "MultiprocessorCount" in text or "multiProcessorCount" in text:
             assert fn == "bi_api.hip", fn
+
+
+def test_layer_step_argument_checks(lib):
+    ok = 1 << 20  # a 16-byte aligned non-null address; never dereferenced on error paths
+    P = ctypes.c_void_p
+    assert lib.bi_embed(None, P(ok), P(ok), 1, 10, 64, None) == -1
+    assert lib.bi_embed(P(ok), P(ok), P(ok), 0, 10, 64, None) == -2
+    assert lib.bi_embed(P(ok), P(ok), P(ok), 1, 10, 60, None) == -3      # H % 8
+    assert lib.bi_rope(P(ok), 512, P(ok), P(ok), P(ok), P(ok), 1, 4, 64, 8, None) == -3  # D
+    assert lib.bi_rope(P(ok), 256, P(ok), P(ok), P(ok), P(ok), 1, 4, 128, 8, None) == -2  # stride
+    assert lib.bi_rope(P(ok), 512, None, P(ok), P(ok), P(ok), 1, 4, 128, 8, None) == -1
+    assert lib.bi_kv_append(P(ok), 1024, P(ok), 1024, P(ok), P(ok), P(ok), 1, 8, 128, 32, 4, 4,
+                            None) == -3                                  # page size
+    assert lib.bi_kv_append(P(ok), 1028, P(ok), 1024, P(ok), P(ok), P(ok), 1, 8, 128, 16, 4, 4,
+                            None) == -3                                  # stride % 8
+    assert lib.bi_kv_append(P(ok), 512, P(ok), 1024, P(ok), P(ok), P(ok), 1, 8, 128, 16, 4, 4,
+                            None) == -2                                  # stride < Hkv*D
+    assert lib.bi_silu_mul(P(ok), P(ok), 1, 12, None) == -3
+    assert lib.bi_silu_mul(P(ok), P(ok), 0, 16, None) == -2
+    assert lib.bi_add(P(ok), P(ok + 2), P(ok), 16, None) == -3
+    assert lib.bi_add(P(ok), P(ok), P(ok), 0, None) == -2
+
+
+def test_rope_table_matches_its_definition(lib):
+    """The host-side table: position 0 is (1, 0); column 0 turns one radian
+    per position (cos 1 and sin 1 to fp32)."""
+    import numpy as np
+    c = np.empty((4, 64), np.float32)
+    s = np.empty_like(c)
+    assert lib.bi_rope_table(5e5, 128, 4, c.ctypes.data, s.ctypes.data) == 0
+    assert np.all(c[0] == 1) and np.all(s[0] == 0)
+    assert c[1, 0] == np.float32(0.5403023058681398) and s[1, 0] == np.float32(0.8414709848078965)
+    assert lib.bi_rope_table(-1.0, 128, 4, c.ctypes.data, s.ctypes.data) == -2
+    assert lib.bi_rope_table(5e5, 127, 4, c.ctypes.data, s.ctypes.data) == -2
