@@ -305,6 +305,7 @@ def main():
         extras["mismatches_m1_vs_batch"] = mism
         extras["rmsnorm"] = bench_rmsnorm(torch, bi, synth, dev, args)
         extras["attention"] = bench_attn(torch, bi, synth, dev, args)
+        extras["verify"] = bench_verify(torch, bi, synth, dev, args)
         result["extras"] = extras
 
     if not args.no_cpu_baseline:
@@ -326,6 +327,52 @@ def bench_rmsnorm(torch, bi, synth, dev, args):
             "overhead_pct": (res["bi"] / res["fast"] - 1) * 100,
             "gbs": byt / (res["bi"] * 1e-6) / 1e9,
             "hbm_frac": byt / (res["bi"] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
+def bench_verify(torch, bi, synth, dev, args):
+    """LLM-42-style grouped verification on the Llama-3-8B-shaped decoder
+    (32 layers, random init): 256 window tokens from 6 requests with prompts
+    of 64..2048 tokens (prompt KV drawn, not prefilled).  Times the grouped
+    forward and counts logits that differ between grouped and alone runs."""
+    import numpy as np
+    from invariant_bi_gemm_02_amd.decoder import Decoder
+    cfg = synth.LLAMA3_8B
+    w = synth.decoder_weights(cfg, seed=11, device=dev)
+    lens = np.random.default_rng(12).integers(64, 2049, 6)
+    sizes = synth.verify_groups(6, 256, seed=13)
+    req = synth.Requests(lens, max_len=int(lens.max()) + 256, vocab=cfg.vocab,
+                         page_size=cfg.page_size, seed=14)
+    dec = Decoder(cfg, w, req.num_pages, 4096, dev)
+    for l, cache in enumerate(dec.kv):
+        cache.copy_(synth.bf16_normal(cache.shape, seed=100 + l, device=dev))
+    rng = np.random.default_rng(15)
+    win = [(r, req.prompt_lens[r] + i, int(rng.integers(0, cfg.vocab)))
+           for r, n in enumerate(sizes) for i in range(n)]
+    win = [win[i] for i in rng.permutation(len(win))]
+    rid, pos, tok = map(np.array, zip(*win))
+    rows = dec.prepare(*req.rows(rid, pos, tok))
+    grouped = dec.run(rows)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        dec.run(rows)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    mism = 0
+    for r in range(len(sizes)):
+        sel = np.nonzero(rid == r)[0]
+        alone = dec.forward(*req.rows(rid[sel], pos[sel], tok[sel]))
+        mism += int((alone.view(torch.int16) != grouped[sel].view(torch.int16)).sum())
+    out = {"config": "Llama-3-8B shape, 32 layers, random init, vocab 128256",
+           "requests": len(sizes), "window_tokens": int(len(win)), "group_sizes": sizes,
+           "prompt_lens": [int(x) for x in lens], "ms_per_verify": ms,
+           "tokens_per_s": len(win) / (ms * 1e-3), "logit_mismatches_grouped_vs_alone": mism}
+    del dec, w, grouped
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_attn(torch, bi, synth, dev, args):

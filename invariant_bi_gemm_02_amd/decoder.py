@@ -30,22 +30,24 @@ class Decoder:
         self.cos, self.sin = bi.rope_table(cfg.theta, cfg.head_dim, max_pos, device)
         self.max_pos = max_pos
 
-    def forward(self, tokens, positions, block_table) -> torch.Tensor:
-        """Logits [M, vocab] (bf16) for rows given as host arrays: tokens [M],
-        positions [M] and block_table [M, max_blocks] (the row's request)."""
-        cfg, w = self.cfg, self.w
-        dev = self.device
+    def prepare(self, tokens, positions, block_table):
+        """Device copies of a forward's row arrays (host arrays in): tokens
+        [M], positions [M], block_table [M, max_blocks] (the row's request)."""
         positions = np.asarray(positions, dtype=np.int32)
         if positions.min() < 0 or positions.max() >= self.max_pos:
             raise ValueError("position outside the rope table")
-        tok = torch.from_numpy(np.ascontiguousarray(tokens, dtype=np.int32)).to(dev)
-        pos = torch.from_numpy(positions).to(dev)
-        ctx = torch.from_numpy(positions + 1).to(dev)           # attend up to itself
-        bt = torch.from_numpy(np.ascontiguousarray(block_table, dtype=np.int32)).to(dev)
-        max_ctx = int(positions.max()) + 1
+        dev = self.device
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+        # a row attends to its request's tokens up to and including itself
+        return (up(tokens), up(positions), up(positions + 1), up(block_table),
+                int(positions.max()) + 1)
+
+    def run(self, rows) -> torch.Tensor:
+        """Logits [M, vocab] (bf16) for rows from prepare()."""
+        cfg, w = self.cfg, self.w
+        tok, pos, ctx, bt, max_ctx = rows
         M = tok.shape[0]
         qd, kd = cfg.q_heads * cfg.head_dim, cfg.kv_heads * cfg.head_dim
-
         h = bi.embed(tok, w["embed"])
         for l in range(cfg.layers):
             x = bi.rmsnorm(h, w[f"{l}.attn_norm"], cfg.eps)
@@ -59,3 +61,7 @@ class Decoder:
             a = bi.silu_mul(bi.gemm(x, w[f"{l}.wgu"]))
             h = bi.add(h, bi.gemm(a, w[f"{l}.wdown"]))
         return bi.gemm(bi.rmsnorm(h, w["final_norm"], cfg.eps), w["lm_head"])
+
+    def forward(self, tokens, positions, block_table) -> torch.Tensor:
+        """prepare() then run(): logits [M, vocab] for host row arrays."""
+        return self.run(self.prepare(tokens, positions, block_table))
