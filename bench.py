@@ -305,6 +305,7 @@ def main():
         extras["mismatches_m1_vs_batch"] = mism
         extras["rmsnorm"] = bench_rmsnorm(torch, bi, synth, dev, args)
         extras["attention"] = bench_attn(torch, bi, synth, dev, args)
+        extras["prefill_attention"] = bench_prefill_attn(torch, bi, synth, dev, args)
         extras["verify"] = bench_verify(torch, bi, synth, dev, args)
         result["extras"] = extras
 
@@ -331,9 +332,11 @@ def bench_rmsnorm(torch, bi, synth, dev, args):
 
 def bench_verify(torch, bi, synth, dev, args):
     """LLM-42-style grouped verification on the Llama-3-8B-shaped decoder
-    (32 layers, random init): 256 window tokens from 6 requests with prompts
-    of 64..2048 tokens (prompt KV drawn, not prefilled).  Times the grouped
-    forward and counts logits that differ between grouped and alone runs."""
+    (32 layers, random init): 6 requests with prompts of 64..2048 tokens are
+    prefilled in one multi-query pass (timed), then 256 window tokens split
+    over them are verified grouped (timed); counts logits that differ
+    between grouped and alone runs, and between the prefill pass and each
+    prompt's last token recomputed alone."""
     import numpy as np
     from invariant_bi_gemm_02_amd.decoder import Decoder
     cfg = synth.LLAMA3_8B
@@ -343,8 +346,25 @@ def bench_verify(torch, bi, synth, dev, args):
     req = synth.Requests(lens, max_len=int(lens.max()) + 256, vocab=cfg.vocab,
                          page_size=cfg.page_size, seed=14)
     dec = Decoder(cfg, w, req.num_pages, 4096, dev)
-    for l, cache in enumerate(dec.kv):
-        cache.copy_(synth.bf16_normal(cache.shape, seed=100 + l, device=dev))
+    segs = [(r, np.arange(n), req.prompts[r]) for r, n in enumerate(req.prompt_lens)]
+    pre_rows = dec.prepare(*synth.grouped_rows(req, segs))
+    prompt_logits = dec.run(pre_rows)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        dec.run(pre_rows)      # rewrites the same K/V bits
+    e1.record()
+    torch.cuda.synchronize()
+    ms_prefill = e0.elapsed_time(e1) / 3
+    last = np.cumsum(req.prompt_lens) - 1
+    pre_mism = 0
+    for r in range(len(segs)):
+        n = req.prompt_lens[r]
+        alone = dec.forward(*req.rows([r], [n - 1], req.prompts[r][-1:]))
+        pre_mism += int((alone.view(torch.int16) !=
+                         prompt_logits[last[r]:last[r] + 1].view(torch.int16)).sum())
+    del prompt_logits
     rng = np.random.default_rng(15)
     win = [(r, req.prompt_lens[r] + i, int(rng.integers(0, cfg.vocab)))
            for r, n in enumerate(sizes) for i in range(n)]
@@ -368,11 +388,50 @@ def bench_verify(torch, bi, synth, dev, args):
         mism += int((alone.view(torch.int16) != grouped[sel].view(torch.int16)).sum())
     out = {"config": "Llama-3-8B shape, 32 layers, random init, vocab 128256",
            "requests": len(sizes), "window_tokens": int(len(win)), "group_sizes": sizes,
-           "prompt_lens": [int(x) for x in lens], "ms_per_verify": ms,
+           "prompt_lens": [int(x) for x in lens],
+           "ms_per_prefill": ms_prefill,
+           "prefill_tokens_per_s": float(np.sum(lens)) / (ms_prefill * 1e-3),
+           "logit_mismatches_prefill_vs_last_token_alone": pre_mism,
+           "ms_per_verify": ms,
            "tokens_per_s": len(win) / (ms * 1e-3), "logit_mismatches_grouped_vs_alone": mism}
     del dec, w, grouped
     torch.cuda.empty_cache()
     return out
+
+
+def bench_prefill_attn(torch, bi, synth, dev, args):
+    """One layer's attention for the rows of six causal prompts (64..2048
+    tokens, Hq 32 / Hkv 8): the multi-query entry point against the decode
+    entry point on the same rows (same bits, per-row K/V reads)."""
+    import numpy as np
+    lens = np.random.default_rng(12).integers(64, 2049, 6).astype(np.int32)
+    _, kv, bt, _ = synth.attn_inputs(lens, seed=21, device=dev)
+    M = int(lens.sum())
+    q = synth.bf16_normal((M, 32, 128), seed=22, device=dev)
+    rid = np.repeat(np.arange(6), lens)
+    ctx = np.concatenate([np.arange(1, L + 1) for L in lens]).astype(np.int32)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    btd, btr, cld = up(bt), up(bt[rid]), up(ctx)
+    rs = up(np.concatenate([[0], np.cumsum(lens)]))
+    mc, mr = int(lens.max()), int(lens.max())
+    outs, res = {}, {}
+    calls = {"prefill": lambda o: bi.paged_prefill_attn(q, kv, btd, rs, cld, mr, max_ctx_len=mc,
+                                                       out=o),
+             "decode": lambda o: bi.paged_decode_attn(q, kv, btr, cld, max_ctx_len=mc, out=o)}
+    for name, fn in calls.items():
+        outs[name] = torch.empty_like(q)
+        fn(outs[name])
+        torch.cuda.synchronize()
+        t = Timer(torch)
+        for _ in range(5):
+            e = t.start()
+            fn(outs[name])
+            t.stop(e)
+        torch.cuda.synchronize()
+        res[name] = t.mean_ms() * 1e3
+    same = bool(torch.equal(outs["prefill"].view(torch.int16), outs["decode"].view(torch.int16)))
+    return {"rows": M, "prompt_lens": [int(x) for x in lens], "prefill_us": res["prefill"],
+            "decode_path_us": res["decode"], "bitwise_equal": same}
 
 
 def bench_attn(torch, bi, synth, dev, args):

@@ -184,6 +184,38 @@ int bi_paged_decode_attn_fast(const bi_bf16 *q, const bi_bf16 *kv_pages,
                               void *stream);
 
 /* ------------------------------------------------------------------------
+ * Multi-query (prefill) attention: many rows of the same requests at once,
+ * each with exactly the decode entry point's per-row schedule, so a row's
+ * output is bitwise what bi_paged_decode_attn gives it (prefill/decode
+ * invariance, the property the LLM-42 digest notes its own method lacks).
+ * Rows of a request share its KV cache; a workgroup loads every K/V tile
+ * once for up to 64/G rows.
+ *
+ * q:           [rows, num_q_heads, head_dim] bf16, rows grouped by request.
+ * kv_pages:    as for bi_paged_decode_attn.
+ * block_table: [requests, max_blocks_per_seq] int32 (one row per REQUEST).
+ * row_start:   [requests + 1] int32 (device): the rows of request r are
+ *              [row_start[r], row_start[r+1]); row_start[0] = 0,
+ *              row_start[requests] = rows, non-decreasing.
+ * ctx_lens:    [rows] int32 (device): row m attends to tokens
+ *              [0, ctx_lens[m]) of its request (position + 1 for causal
+ *              prefill); <= 0 gives zeros.
+ * out:         [rows, num_q_heads, head_dim] bf16.
+ * d:           as for bi_paged_decode_attn with d->batch = rows.
+ * requests:    number of requests R; max_rows_per_request: an upper bound on
+ *              row_start[r+1] - row_start[r] (sizes the grid).
+ * ws:          at least bi_attn_workspace_bytes(d) bytes.
+ * Same requirements as bi_paged_decode_attn, and requests *
+ * ceil(max_rows_per_request / (64 / G)) <= 65535.
+ * ---------------------------------------------------------------------- */
+int bi_paged_prefill_attn(const bi_bf16 *q, const bi_bf16 *kv_pages,
+                          const int32_t *block_table, const int32_t *row_start,
+                          const int32_t *ctx_lens, bi_bf16 *out,
+                          const bi_attn_desc *d, int32_t requests,
+                          int32_t max_rows_per_request, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Element-wise steps of a Llama-style decoder layer built around the three
  * calls above.  [LLM-42] problem statement: a token's logits must come out
  * the same whether it is verified alone or grouped with other requests, so

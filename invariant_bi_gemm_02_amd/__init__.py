@@ -26,4 +26,5 @@ from ._lib import (  # noqa: F401
     kv_append,
     silu_mul,
     add,
+    paged_prefill_attn,
 )

@@ -37,7 +37,7 @@ EXPORTS = ("bi_version", "bi_status_string", "bi_gemm_workspace_bytes", "bi_gemm
            "bi_gemm_fast_workspace_bytes", "bi_gemm_fast", "bi_rmsnorm", "bi_rmsnorm_fast",
            "bi_attn_workspace_bytes", "bi_paged_decode_attn", "bi_attn_fast_workspace_bytes",
            "bi_paged_decode_attn_fast", "bi_embed", "bi_rope_table", "bi_rope", "bi_kv_append",
-           "bi_silu_mul", "bi_add")
+           "bi_silu_mul", "bi_add", "bi_paged_prefill_attn")
 
 _lock = threading.Lock()
 _lib = None
@@ -83,6 +83,8 @@ def load(path: str | None = None):
             "bi_kv_append": [vp, i64, vp, i64, vp, vp, vp, i64, i32, i32, i32, i32, i64, vp],
             "bi_silu_mul": [vp, vp, i64, i64, vp],
             "bi_add": [vp, vp, vp, i64, vp],
+            "bi_paged_prefill_attn": [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AttnDesc), i32, i32,
+                                      vp, sz, vp],
         }
         for f, a in sigs.items():
             getattr(lib, f).restype = ctypes.c_int
@@ -209,12 +211,12 @@ def rmsnorm_fast(x, g, eps: float = 1e-5, out=None):
     return _rmsnorm("bi_rmsnorm_fast", x, g, eps, out)
 
 
-def _attn_desc(q, kv, block_table, max_ctx_len, scale):
+def _attn_desc(q, kv, block_table, max_ctx_len, scale, table_rows=None):
     B, Hq, D = q.shape
     P, two, Hkv, PS, D2 = kv.shape
     if two != 2 or D2 != D:
         raise ValueError("kv_pages must be [P, 2, Hkv, page_size, head_dim]")
-    if block_table.dim() != 2 or block_table.shape[0] != B:
+    if block_table.dim() != 2 or block_table.shape[0] != (B if table_rows is None else table_rows):
         raise ValueError("block_table must be [batch, max_blocks]")
     if scale is None:
         scale = float(torch.tensor(1.0, dtype=torch.float32) /
@@ -364,4 +366,40 @@ def add(a, b, out=None):
         out = torch.empty_like(a)
     _raise(lib.bi_add(a.data_ptr(), b.data_ptr(), out.data_ptr(), a.numel(), _stream(a.device)),
            "bi_add")
+    return out
+
+
+def paged_prefill_attn(q, kv_pages, block_table, row_start, ctx_lens, max_rows_per_request=None,
+                       max_ctx_len=None, scale=None, out=None, ws: Workspace | None = None):
+    """Multi-query attention for rows grouped by request (block_table has one
+    row per request, row_start [R+1] delimits each request's rows); every row
+    gets bitwise the decode entry point's result.  max_rows_per_request
+    defaults to the largest request (read back from row_start)."""
+    lib = load()
+    if max_rows_per_request is None:
+        max_rows_per_request = int((row_start[1:] - row_start[:-1]).max().item())
+    _check_bf16(q, "q", 3)
+    _check_bf16(kv_pages, "kv_pages", 5)
+    for t, n in ((block_table, "block_table"), (row_start, "row_start"), (ctx_lens, "ctx_lens")):
+        _check_i32(t, n)
+    if ctx_lens.shape[0] != q.shape[0]:
+        raise ValueError("ctx_lens must be [rows]")
+    if max_ctx_len is None:
+        max_ctx_len = int(ctx_lens.max().item())
+    if row_start.shape[0] != block_table.shape[0] + 1:
+        raise ValueError("row_start must be [requests + 1]")
+    # the descriptor's batch is the number of rows; the block table has one
+    # row per request
+    desc = _attn_desc(q, kv_pages, block_table, max(int(max_ctx_len), 1), scale,
+                      table_rows=row_start.shape[0] - 1)
+    if out is None:
+        out = torch.empty_like(q)
+    need = int(lib.bi_attn_workspace_bytes(ctypes.byref(desc)))
+    buf = _ws_for(q.device, ws).get(need)
+    st = lib.bi_paged_prefill_attn(q.data_ptr(), kv_pages.data_ptr(), block_table.data_ptr(),
+                                   row_start.data_ptr(), ctx_lens.data_ptr(), out.data_ptr(),
+                                   ctypes.byref(desc), block_table.shape[0],
+                                   int(max_rows_per_request), buf.data_ptr(), buf.numel(),
+                                   _stream(q.device))
+    _raise(st, "bi_paged_prefill_attn")
     return out

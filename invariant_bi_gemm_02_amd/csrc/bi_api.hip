@@ -182,6 +182,24 @@ int bi_paged_decode_attn_fast(const bi_bf16* q, const bi_bf16* kv_pages,
   return attn_entry(q, kv_pages, block_table, ctx_lens, out, d, ws, ws_bytes, stream, true);
 }
 
+int bi_paged_prefill_attn(const bi_bf16* q, const bi_bf16* kv_pages, const int32_t* block_table,
+                          const int32_t* row_start, const int32_t* ctx_lens, bi_bf16* out,
+                          const bi_attn_desc* d, int32_t requests, int32_t max_rows_per_request,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (!row_start) return BI_ERR_NULL;
+  int st = check_attn(q, kv_pages, block_table, ctx_lens, out, d);
+  if (st != BI_OK) return st;
+  if (requests <= 0 || max_rows_per_request <= 0 || max_rows_per_request > d->batch)
+    return BI_ERR_SHAPE;
+  if ((int64_t)requests * d->max_blocks_per_seq >= kMaxElems) return BI_ERR_SHAPE;
+  if ((uintptr_t)row_start & 3u) return BI_ERR_UNSUPPORTED;
+  const size_t need = bi::attn_ws_bytes(d, false, 0);
+  if (!ws || ws_bytes < need) return BI_ERR_WORKSPACE;
+  if (!aligned16(ws)) return BI_ERR_UNSUPPORTED;
+  return bi::launch_prefill_attn(q, kv_pages, block_table, row_start, ctx_lens, out, d, requests,
+                                 max_rows_per_request, ws, ws_bytes, (hipStream_t)stream);
+}
+
 int bi_embed(const int32_t* tokens, const bi_bf16* table, bi_bf16* out, int64_t M, int64_t V,
              int64_t H, void* stream) {
   if (!tokens || !table || !out) return BI_ERR_NULL;

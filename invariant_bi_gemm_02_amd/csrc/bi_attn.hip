@@ -225,6 +225,263 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Multi-query (prefill) chunk kernel: the rows of one request share its KV
+// cache, so a workgroup takes QB = 64/G consecutive rows of a request (64
+// (row, q head) columns) and one chunk, loads each K/V tile once for all of
+// them, and gives every (row, head) exactly the decode kernel's computation:
+// the same score instruction on the same operands (an output element of the
+// matrix-core product does not depend on the other columns), the same tile
+// maxima (a maximum does not depend on order), exponentials and in-order
+// chains over the row's own tokens (t < ctx_lens[row]), and the same partial
+// layout for the combine.  So a row's output is bitwise the one the decode
+// entry point gives it.
+//
+// Wave w owns columns 16w .. 16w+15.  Scores and softmax run with lane l
+// holding column l % 16 (the matrix-core output layout: 16 of the tile's
+// tokens per lane); the P V chains run with lane = pair of dims and all 16
+// columns advanced together per token, so V is read from LDS once per token
+// for 16 columns.  Tokens that every column of the wave takes run without
+// masks; the few past the shortest row (the causal diagonal) run per row.
+// grid = (max chunks, num_kv_heads, requests * row blocks), block = 256.
+template <int G>
+__global__ __launch_bounds__(256) void attn_prefill_chunk_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ row_start,
+    const int32_t* __restrict__ ctx_lens, float* __restrict__ part, int Hq, int Hkv,
+    int max_blocks, long long num_pages, int max_ctx, int nc_stride, int row_blocks, int rows,
+    float scale) {
+  constexpr int QB = 64 / G;   // rows per workgroup
+  constexpr int RPW = 16 / G;  // rows per wave
+  __shared__ __attribute__((aligned(16))) uint16_t ks[ATILE * AKLD];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[ATILE * AD];
+  __shared__ __attribute__((aligned(16))) float pw[4][ATILE][16];  // per wave: [token][column]
+  __shared__ int pgs[ACHUNK / APS];
+  __shared__ int lens[QB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int r = blockIdx.z / row_blocks;
+  const int rb = blockIdx.z % row_blocks;
+  // rows outside [0, rows) are never touched, whatever row_start holds
+  const long long rs = min(max(0, (int)row_start[r]), rows);
+  const long long re = min(max((int)rs, (int)row_start[r + 1]), rows);
+  const long long row0l = rs + (long long)rb * QB;
+  if (row0l >= re) return;
+  const int row0 = (int)row0l;
+  const int nrows = (int)min((long long)QB, re - row0l);
+  const int t_begin = c * ACHUNK;
+  int lmax = 0;
+  for (int i = 0; i < nrows; ++i) lmax = max(lmax, min((int)ctx_lens[row0 + i], max_ctx));
+  if (t_begin >= lmax) return;
+  const int t_end = min(lmax, t_begin + ACHUNK);
+  const int32_t* bt = block_table + (size_t)r * max_blocks;
+
+  if (tid < QB) lens[tid] = tid < nrows ? min((int)ctx_lens[row0 + tid], max_ctx) : 0;
+  if (tid < (t_end - t_begin + APS - 1) / APS) pgs[tid] = bt[t_begin / APS + tid];
+
+  // this lane's column in the score layout, and its q as the B operand
+  const int cl = lane & 15;
+  const int col = 16 * wave + cl;
+  const bool wave_live = 16 * wave < nrows * G;
+  u32x4_t bq[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+    bq[kb] = col / G < nrows
+                 ? ldg128(q + ((size_t)(row0 + col / G) * Hq + hk * G + col % G) * AD + kb * 32 +
+                          (lane >> 4) * 8)
+                 : u32x4_t{0u, 0u, 0u, 0u};
+  __syncthreads();
+  const int my_len = lens[col / G];
+
+  u32x4_t kr[4], vr[4];
+  auto load_tile = [&](int t0, int nt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = tid + 256 * i;
+      const int tt = ci >> 4;
+      const int dc = ci & 15;
+      kr[i] = u32x4_t{0u, 0u, 0u, 0u};
+      vr[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (tt < nt) {
+        const int t = t0 + tt;
+        const long long page = pgs[(t - t_begin) / APS];
+        if (page >= 0 && page < num_pages) {
+          const size_t kofs = (((size_t)page * 2 + 0) * Hkv + hk) * (APS * AD) + (t % APS) * AD + dc * 8;
+          const size_t vofs = kofs + (size_t)Hkv * APS * AD;
+          kr[i] = ldg128(kv + kofs);
+          vr[i] = ldg128(kv + vofs);
+        }
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = tid + 256 * i;
+      const int tt = ci >> 4;
+      const int dc = ci & 15;
+      *(u32x4_t*)&ks[tt * AKLD + dc * 8] = kr[i];
+      *(u32x4_t*)&vs[tt * AD + dc * 8] = vr[i];
+    }
+  };
+
+  float m_c = -INFINITY, l_c = 0.0f;  // per column (score layout)
+  float a0[16], a1[16];               // per column (dims 2 lane, 2 lane + 1)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    a0[j] = 0.0f;
+    a1[j] = 0.0f;
+  }
+  const uint32_t* vcol = (const uint32_t*)vs + lane;
+  const float* pwv = &pw[wave][0][0];
+
+  load_tile(t_begin, min(ATILE, t_end - t_begin));
+  for (int t0 = t_begin; t0 < t_end; t0 += ATILE) {
+    const int nt = min(ATILE, t_end - t0);
+    __syncthreads();  // previous tile fully consumed
+    store_tile();
+    __syncthreads();
+    const int t1 = t0 + ATILE;
+    if (t1 < t_end) load_tile(t1, min(ATILE, t_end - t1));
+    if (!wave_live) continue;
+
+    // scores S^T = K Q^T for the tile's 64 tokens x the wave's 16 columns
+    const int nt_c = min(nt, my_len - t0);  // this column's tokens in the tile
+    f32x4_t sc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      sc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* krow = ks + (16 * tt + cl) * AKLD + (lane >> 4) * 8;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        sc[tt] = mfma16x16x32(*(const u32x4_t*)(krow + kb * 32), bq[kb], sc[tt]);
+    }
+    float s[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = 16 * tt + (lane >> 4) * 4 + e;
+        const float sv = sc[tt][e] * scale;
+        s[4 * tt + e] = tok < nt_c ? sv : -INFINITY;
+        mt = fmaxf(mt, s[4 * tt + e]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const bool live = nt_c > 0;
+    const float mn = fmaxf(m_c, mt);
+    const float alpha = (m_c == -INFINITY) ? 0.0f : __expf(m_c - mn);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = 16 * tt + (lane >> 4) * 4 + e;
+        pw[wave][tok][cl] = tok < nt_c ? __expf(s[4 * tt + e] - mn) : 0.0f;
+      }
+    if (live) {
+      l_c = l_c * alpha;
+      m_c = mn;
+    }
+    // tokens taken by every column of the wave, and by the longest
+    int ntc = max(nt_c, 0), nmin = ntc, nmax = ntc;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      nmin = min(nmin, __shfl_xor(nmin, o, 64));
+      nmax = max(nmax, __shfl_xor(nmax, o, 64));
+    }
+    nmin = __builtin_amdgcn_readfirstlane(nmin);
+    nmax = __builtin_amdgcn_readfirstlane(nmax);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (__builtin_amdgcn_readlane(ntc, j) > 0) {
+        const float aj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), j));
+        a0[j] = a0[j] * aj;
+        a1[j] = a1[j] * aj;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+    // all 16 columns, tokens [0, nmin), in token order
+    int i = 0;
+    for (; i + 4 <= nmin; i += 4) {
+      uint32_t v2[4];
+      float pl[4];
+      f32x4_t p[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v2[u] = vcol[(i + u) * (AD / 2)];
+        pl[u] = pwv[(i + u) * 16 + cl];
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) p[u][qd] = *(const f32x4_t*)(pwv + (i + u) * 16 + 4 * qd);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        l_c = l_c + pl[u];
+        const float lo = bf16_lo(v2[u]), hi = bf16_hi(v2[u]);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          a0[j] = __fmaf_rn(p[u][j >> 2][j & 3], lo, a0[j]);
+          a1[j] = __fmaf_rn(p[u][j >> 2][j & 3], hi, a1[j]);
+        }
+      }
+    }
+    for (; i < nmin; ++i) {
+      const uint32_t v2 = vcol[i * (AD / 2)];
+      l_c = l_c + pwv[i * 16 + cl];
+      const float lo = bf16_lo(v2), hi = bf16_hi(v2);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float pj = pwv[i * 16 + j];
+        a0[j] = __fmaf_rn(pj, lo, a0[j]);
+        a1[j] = __fmaf_rn(pj, hi, a1[j]);
+      }
+    }
+    // the rest of each column's tokens [nmin, nt_c), in order
+    for (int k = nmin; k < nmax; ++k) {
+      const float pk = pwv[k * 16 + cl];
+      if (k < nt_c) l_c = l_c + pk;
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int nt_r = __builtin_amdgcn_readlane(ntc, rr * G);  // same for the row's G heads
+      for (int k = nmin; k < nt_r; ++k) {
+        const uint32_t v2 = vcol[k * (AD / 2)];
+        const float lo = bf16_lo(v2), hi = bf16_hi(v2);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pj = pwv[k * 16 + rr * G + h];
+          a0[rr * G + h] = __fmaf_rn(pj, lo, a0[rr * G + h]);
+          a1[rr * G + h] = __fmaf_rn(pj, hi, a1[rr * G + h]);
+        }
+      }
+    }
+  }
+
+  // partials of the rows whose context reaches this chunk: [row][h][c][...]
+  if (!wave_live) return;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int cj = 16 * wave + j;
+    const int rr = cj / G;
+    if (rr < nrows && lens[rr] > t_begin) {
+      float* pp = part + (((size_t)(row0 + rr) * Hq + hk * G + cj % G) * nc_stride + c) * APART;
+      if (lane == j) {
+        pp[0] = m_c;
+        pp[1] = l_c;
+      }
+      pp[4 + 2 * lane] = a0[j];
+      pp[5 + 2 * lane] = a1[j];
+    }
+  }
+}
+
 // grid = (num_q_heads, batch), block = 128 (one lane per dim).
 // The chunk maxima and weights are computed by all lanes in parallel (the
 // maximum does not depend on order); the two sums then run in chunk order,
@@ -342,6 +599,39 @@ int launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* block_tabl
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)d->num_q_heads, (unsigned)d->batch),
                      dim3(128), 0, stream, part, ctx_lens, out, d->num_q_heads, d->max_ctx_len,
                      ncs, fixed, splits);
+  return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+int launch_prefill_attn(const uint16_t* q, const uint16_t* kv, const int32_t* block_table,
+                        const int32_t* row_start, const int32_t* ctx_lens, uint16_t* out,
+                        const bi_attn_desc* d, int requests, int max_rows_per_request, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const int ncs = nc_stride_of(d, false, 0);
+  if (ws_bytes < attn_ws_bytes(d, false, 0)) return BI_ERR_WORKSPACE;
+  const int qb = 64 / G;
+  const long long row_blocks = (max_rows_per_request + qb - 1) / qb;
+  if (ncs > 65535 || d->num_kv_heads > 65535 || (long long)requests * row_blocks > 65535)
+    return BI_ERR_UNSUPPORTED;
+  float* part = (float*)ws;
+  dim3 grid((unsigned)ncs, (unsigned)d->num_kv_heads, (unsigned)(requests * row_blocks));
+#define BI_PREFILL_LAUNCH(GG)                                                                  \
+  hipLaunchKernelGGL(attn_prefill_chunk_kernel<GG>, grid, dim3(256), 0, stream, q, kv,       \
+                     block_table, row_start, ctx_lens, part, d->num_q_heads, d->num_kv_heads, \
+                     d->max_blocks_per_seq, (long long)d->num_pages, d->max_ctx_len, ncs,     \
+                     (int)row_blocks, d->batch, d->scale)
+  switch (G) {
+    case 1: BI_PREFILL_LAUNCH(1); break;
+    case 2: BI_PREFILL_LAUNCH(2); break;
+    case 4: BI_PREFILL_LAUNCH(4); break;
+    case 8: BI_PREFILL_LAUNCH(8); break;
+    default: return BI_ERR_UNSUPPORTED;
+  }
+#undef BI_PREFILL_LAUNCH
+  if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)d->num_q_heads, (unsigned)d->batch),
+                     dim3(128), 0, stream, part, ctx_lens, out, d->num_q_heads, d->max_ctx_len,
+                     ncs, ACHUNK, 0);
   return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 

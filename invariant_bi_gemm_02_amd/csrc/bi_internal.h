@@ -26,6 +26,11 @@ int launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* block_tabl
                 const int32_t* ctx_lens, uint16_t* out, const bi_attn_desc* d, void* ws,
                 size_t ws_bytes, hipStream_t stream, bool fast, int num_cus);
 
+int launch_prefill_attn(const uint16_t* q, const uint16_t* kv, const int32_t* block_table,
+                        const int32_t* row_start, const int32_t* ctx_lens, uint16_t* out,
+                        const bi_attn_desc* d, int requests, int max_rows_per_request, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
 // Decoder-layer element-wise steps (bi_layer.hip)
 int launch_embed(const int32_t* tokens, const uint16_t* table, uint16_t* out, int64_t M,
                  int64_t V, int64_t H, hipStream_t stream);

@@ -9,7 +9,8 @@ cache up to and including itself, so a batch may mix any number of requests
 and window lengths -- the LLM-42 digest's grouped verification, where the
 tokens of several requests are checked in one fixed-shape pass.  Since every
 call is row-independent, a row's logits are bit-identical whether it is run
-alone, with the rest of its request, or grouped with other requests.
+alone, with the rest of its request, or grouped with other requests, and
+whether its prompt was prefilled in one pass, in chunks or token by token.
 """
 from __future__ import annotations
 
@@ -30,22 +31,37 @@ class Decoder:
         self.cos, self.sin = bi.rope_table(cfg.theta, cfg.head_dim, max_pos, device)
         self.max_pos = max_pos
 
-    def prepare(self, tokens, positions, block_table):
+    def prepare(self, tokens, positions, block_table, row_start=None):
         """Device copies of a forward's row arrays (host arrays in): tokens
-        [M], positions [M], block_table [M, max_blocks] (the row's request)."""
+        [M], positions [M], block_table [M, max_blocks] (the row's request).
+
+        With row_start ([R + 1], host) the rows come grouped by request --
+        rows row_start[r] .. row_start[r+1]-1 belong to request r, and
+        block_table has one row per request ([R, max_blocks]) -- and the
+        attention runs the multi-query entry point, which loads a request's
+        K/V once for many rows and gives each row the same bits as the
+        per-row path."""
         positions = np.asarray(positions, dtype=np.int32)
         if positions.min() < 0 or positions.max() >= self.max_pos:
             raise ValueError("position outside the rope table")
         dev = self.device
         up = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+        grouped = None
+        if row_start is not None:
+            row_start = np.asarray(row_start, dtype=np.int32)
+            counts = np.diff(row_start)
+            if row_start[0] != 0 or row_start[-1] != len(positions) or (counts < 0).any():
+                raise ValueError("row_start must run from 0 to the number of rows")
+            grouped = (up(block_table), up(row_start), int(counts.max()))
+            block_table = np.repeat(np.asarray(block_table), counts, axis=0)
         # a row attends to its request's tokens up to and including itself
         return (up(tokens), up(positions), up(positions + 1), up(block_table),
-                int(positions.max()) + 1)
+                int(positions.max()) + 1, grouped)
 
     def run(self, rows) -> torch.Tensor:
         """Logits [M, vocab] (bf16) for rows from prepare()."""
         cfg, w = self.cfg, self.w
-        tok, pos, ctx, bt, max_ctx = rows
+        tok, pos, ctx, bt, max_ctx, grouped = rows
         M = tok.shape[0]
         qd, kd = cfg.q_heads * cfg.head_dim, cfg.kv_heads * cfg.head_dim
         h = bi.embed(tok, w["embed"])
@@ -55,13 +71,17 @@ class Decoder:
             q = bi.rope(qkv[:, :qd], cfg.q_heads, pos, self.cos, self.sin)
             k = bi.rope(qkv[:, qd:qd + kd], cfg.kv_heads, pos, self.cos, self.sin)
             bi.kv_append(k.view(M, kd), qkv[:, qd + kd:], self.kv[l], bt, pos)
-            att = bi.paged_decode_attn(q, self.kv[l], bt, ctx, max_ctx_len=max_ctx)
+            if grouped is None:
+                att = bi.paged_decode_attn(q, self.kv[l], bt, ctx, max_ctx_len=max_ctx)
+            else:
+                att = bi.paged_prefill_attn(q, self.kv[l], grouped[0], grouped[1], ctx,
+                                            grouped[2], max_ctx_len=max_ctx)
             h = bi.add(h, bi.gemm(att.view(M, qd), w[f"{l}.wo"]))
             x = bi.rmsnorm(h, w[f"{l}.ffn_norm"], cfg.eps)
             a = bi.silu_mul(bi.gemm(x, w[f"{l}.wgu"]))
             h = bi.add(h, bi.gemm(a, w[f"{l}.wdown"]))
         return bi.gemm(bi.rmsnorm(h, w["final_norm"], cfg.eps), w["lm_head"])
 
-    def forward(self, tokens, positions, block_table) -> torch.Tensor:
+    def forward(self, tokens, positions, block_table, row_start=None) -> torch.Tensor:
         """prepare() then run(): logits [M, vocab] for host row arrays."""
-        return self.run(self.prepare(tokens, positions, block_table))
+        return self.run(self.prepare(tokens, positions, block_table, row_start))

@@ -212,6 +212,17 @@ class Requests:
                 np.ascontiguousarray(self.block_table[req_ids]))
 
 
+def grouped_rows(req: "Requests", segments):
+    """Rows of a multi-query forward from segments [(request, positions,
+    tokens)], each one request's run of rows: tokens [M], positions [M], the
+    segments' block table rows [S, max_blocks] and row_start [S + 1]."""
+    tok = np.concatenate([np.asarray(s[2], np.int32) for s in segments])
+    pos = np.concatenate([np.asarray(s[1], np.int32) for s in segments])
+    bt = np.ascontiguousarray(req.block_table[[s[0] for s in segments]])
+    row_start = np.concatenate([[0], np.cumsum([len(s[1]) for s in segments])]).astype(np.int32)
+    return tok, pos, bt, row_start
+
+
 def verify_groups(n_requests: int, total: int, seed: int):
     """LLM-42-style grouped verification: split `total` window tokens over
     the requests (each gets at least one), in a shuffled row order."""

@@ -100,6 +100,14 @@ def test_attention_argument_checks(lib):
     bad = _lib.AttnDesc(4, 24, 8, 128, 16, 64, 1000, 1024, 0.088)      # group of 3
     assert lib.bi_paged_decode_attn(*args, ctypes.byref(bad), P(ok), 1 << 30, None) == -3
     assert lib.bi_paged_decode_attn(None, *args[1:], ctypes.byref(d), P(ok), need, None) == -1
+    # multi-query entry: [rows] q with a [requests] block table and row_start
+    pre = [P(ok), P(ok), P(ok), P(ok), P(ok), P(ok)]
+    assert lib.bi_paged_prefill_attn(*pre, ctypes.byref(d), 2, 4, P(ok), need - 4, None) == -4
+    assert lib.bi_paged_prefill_attn(*pre[:3], None, *pre[4:], ctypes.byref(d), 2, 4, P(ok),
+                                     need, None) == -1
+    assert lib.bi_paged_prefill_attn(*pre, ctypes.byref(d), 0, 4, P(ok), need, None) == -2
+    assert lib.bi_paged_prefill_attn(*pre, ctypes.byref(d), 2, 5, P(ok), need, None) == -2
+    assert lib.bi_paged_prefill_attn(*pre, ctypes.byref(bad), 2, 4, P(ok), need, None) == -3
 
 
 def test_static_lint_no_float_atomics_or_cu_count_in_invariant_paths():

@@ -141,3 +141,86 @@ def test_llama3_8b_grouped_verification_is_bitwise(gpu):
     # one token alone as well
     one = dec.forward(*req.rows(rid[:1], pos[:1], tok[:1]))
     assert torch.equal(one.view(torch.int16), grouped[:1].view(torch.int16))
+
+
+def test_small_decoder_prefill_one_pass_chunked_and_token_by_token(gpu):
+    """Query-length invariance through the whole stack: the prompts' logits
+    are the same bits prefilled in one multi-query pass, in chunks that cut
+    across requests, and one token per forward; and the one-pass logits stay
+    within the tiny-decoder rule of the oracle."""
+    cfg = synth.TINY
+    w = synth.decoder_weights(cfg, seed=16, device=DEV)
+    req = synth.Requests([45, 20, 33], max_len=64, vocab=cfg.vocab, page_size=16, seed=17)
+    segs = [(r, np.arange(n), req.prompts[r]) for r, n in enumerate(req.prompt_lens)]
+    one = Decoder(cfg, w, req.num_pages, 64)
+    whole = bits(one.forward(*synth.grouped_rows(req, segs)))
+    # chunks of 19 rows: each chunk's segments are pieces of the prompts
+    chunked = Decoder(cfg, w, req.num_pages, 64)
+    flat = [(r, p, t) for r, ps, ts in segs for p, t in zip(ps, ts)]
+    got = []
+    for s in range(0, len(flat), 19):
+        part = flat[s:s + 19]
+        pieces = []
+        for r, p, t in part:
+            if pieces and pieces[-1][0] == r:
+                pieces[-1][1].append(p)
+                pieces[-1][2].append(t)
+            else:
+                pieces.append((r, [p], [t]))
+        got.append(bits(chunked.forward(*synth.grouped_rows(req, pieces))))
+    np.testing.assert_array_equal(np.concatenate(got), whole)
+    # token by token, per-row attention path
+    single = Decoder(cfg, w, req.num_pages, 64)
+    toks = []
+    for r, p, t in flat:
+        toks.append(bits(single.forward(*req.rows([r], [p], [t]))))
+    np.testing.assert_array_equal(np.concatenate(toks), whole)
+    ora = OracleDecoder(cfg, {k: bits(v) for k, v in w.items()}, req.num_pages, 64)
+    rid, pos, tok = map(np.array, zip(*flat))
+    want = ora.forward(*req.rows(rid, pos, tok))
+    g, r = bits_to_f64(whole), bits_to_f64(want)
+    rel = np.abs(g - r) / np.max(np.abs(r), axis=1, keepdims=True)
+    assert rel.max() <= 2.0 ** -6 and rel.mean() <= 2.0 ** -11, (rel.max(), rel.mean())
+
+
+def test_llama3_8b_prefill_is_query_length_invariant(gpu):
+    """The Llama-3-8B-shaped decoder: six prompts (1..700 tokens) prefilled
+    in one multi-query pass and in 128-row chunks give the same logits;
+    sampled prompt rows recomputed alone (per-row path, M = 1) match; and a
+    grouped verify window over the real prefilled cache matches its
+    per-request runs."""
+    cfg = synth.LLAMA3_8B
+    w = synth.decoder_weights(cfg, seed=18, device=DEV)
+    lens = np.array([1, 700, 129, 64, 300, 17])
+    req = synth.Requests(lens, max_len=int(lens.max()) + 64, vocab=cfg.vocab, page_size=16,
+                         seed=19)
+    segs = [(r, np.arange(n), req.prompts[r]) for r, n in enumerate(req.prompt_lens)]
+    a = Decoder(cfg, w, req.num_pages, 1024)
+    whole = a.forward(*synth.grouped_rows(req, segs))
+    b = Decoder(cfg, w, req.num_pages, 1024)
+    flat = [(r, p, t) for r, ps, ts in segs for p, t in zip(ps, ts)]
+    for s in range(0, len(flat), 128):
+        part = flat[s:s + 128]
+        pieces = []
+        for r, p, t in part:
+            if pieces and pieces[-1][0] == r:
+                pieces[-1][1].append(p)
+                pieces[-1][2].append(t)
+            else:
+                pieces.append((r, [p], [t]))
+        got = b.forward(*synth.grouped_rows(req, pieces))
+        assert torch.equal(got.view(torch.int16), whole[s:s + len(part)].view(torch.int16)), s
+    for m in np.random.default_rng(20).choice(len(flat), 6, replace=False):
+        r, p, t = flat[m]
+        alone = a.forward(*req.rows([r], [p], [t]))
+        assert torch.equal(alone.view(torch.int16), whole[m:m + 1].view(torch.int16)), m
+    # verify windows after the prompts, over the prefilled cache
+    sizes = synth.verify_groups(6, 64, seed=21)
+    _, win = _prefill_and_window(req, 22, sizes)
+    rid, pos, tok = map(np.array, zip(*win))
+    tok = tok % cfg.vocab
+    grouped = a.forward(*req.rows(rid, pos, tok))
+    for r in range(6):
+        sel = np.nonzero(rid == r)[0]
+        alone = a.forward(*req.rows(rid[sel], pos[sel], tok[sel]))
+        assert torch.equal(alone.view(torch.int16), grouped[sel].view(torch.int16)), f"req {r}"
