@@ -35,6 +35,7 @@ static constexpr int ACHUNK = 256;    // tokens per chunk (batch-invariant entry
 static constexpr int APART = AD + 4;  // floats per partial: m, l, 2 pad, acc[128]
 static constexpr int AKLD = AD + 8;   // padded K row in LDS (elements)
 static constexpr int ACH = 256;       // longest chunk the fast twin may pick (combine bound)
+static constexpr int ACOMB_MAXC = 1024;  // chunks per request the combine handles
 
 // Chunk length for request length L: fixed, or (fast twin) from the split count.
 __device__ __forceinline__ int chunk_len(int L, int fixed_chunk, int splits) {
@@ -228,8 +229,9 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
 // ---------------------------------------------------------------------------
 // Multi-query (prefill) chunk kernel: the rows of one request share its KV
 // cache, so a workgroup takes QB = 64/G consecutive rows of a request (64
-// (row, q head) columns) and one chunk, loads each K/V tile once for all of
-// them, and gives every (row, head) exactly the decode kernel's computation:
+// (row, q head) columns) and walks the chunks their contexts reach, loading
+// each K/V tile once for all of them.  Every (row, head) gets exactly the
+// decode kernel's computation for each chunk:
 // the same score instruction on the same operands (an output element of the
 // matrix-core product does not depend on the other columns), the same tile
 // maxima (a maximum does not depend on order), exponentials and in-order
@@ -243,29 +245,34 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
 // columns advanced together per token, so V is read from LDS once per token
 // for 16 columns.  Tokens that every column of the wave takes run without
 // masks; the few past the shortest row (the causal diagonal) run per row.
-// grid = (max chunks, num_kv_heads, requests * row blocks), block = 256.
+// Chunks start on tile boundaries (256 = 4 x 64), so the walk is one tile
+// loop that restarts the online softmax at each chunk start and writes the
+// chunk's partials at its end.  grid = num_kv_heads * requests * row blocks
+// (1-D), block = 256; the kv head varies fastest (equal work per XCD, which
+// take workgroups round-robin), and the row blocks come last-first, so that
+// the longest contexts start first.
 template <int G>
-__global__ __launch_bounds__(256) void attn_prefill_chunk_kernel(
+__global__ __launch_bounds__(256, 3) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ row_start,
-    const int32_t* __restrict__ ctx_lens, float* __restrict__ part, int Hq, int Hkv,
-    int max_blocks, long long num_pages, int max_ctx, int nc_stride, int row_blocks, int rows,
-    float scale) {
+    const int32_t* __restrict__ ctx_lens, float* __restrict__ part, uint16_t* __restrict__ out,
+    int Hq, int Hkv, int requests, int max_blocks, long long num_pages, int max_ctx,
+    int nc_stride, int row_blocks, int rows, float scale) {
   constexpr int QB = 64 / G;   // rows per workgroup
   constexpr int RPW = 16 / G;  // rows per wave
+  constexpr int PU = 1;        // tokens per step of the P V loop
   __shared__ __attribute__((aligned(16))) uint16_t ks[ATILE * AKLD];
   __shared__ __attribute__((aligned(16))) uint16_t vs[ATILE * AD];
   __shared__ __attribute__((aligned(16))) float pw[4][ATILE][16];  // per wave: [token][column]
-  __shared__ int pgs[ACHUNK / APS];
   __shared__ int lens[QB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int c = blockIdx.x;
-  const int hk = blockIdx.y;
-  const int r = blockIdx.z / row_blocks;
-  const int rb = blockIdx.z % row_blocks;
+  const int hk = (int)(blockIdx.x % (unsigned)Hkv);
+  const int z = (int)(blockIdx.x / (unsigned)Hkv);
+  const int r = z % requests;
+  const int rb = row_blocks - 1 - z / requests;
   // rows outside [0, rows) are never touched, whatever row_start holds
   const long long rs = min(max(0, (int)row_start[r]), rows);
   const long long re = min(max((int)rs, (int)row_start[r + 1]), rows);
@@ -273,15 +280,16 @@ __global__ __launch_bounds__(256) void attn_prefill_chunk_kernel(
   if (row0l >= re) return;
   const int row0 = (int)row0l;
   const int nrows = (int)min((long long)QB, re - row0l);
-  const int t_begin = c * ACHUNK;
-  int lmax = 0;
-  for (int i = 0; i < nrows; ++i) lmax = max(lmax, min((int)ctx_lens[row0 + i], max_ctx));
-  if (t_begin >= lmax) return;
-  const int t_end = min(lmax, t_begin + ACHUNK);
+  // the block's longest context: one load per lane, then a wave maximum
+  const int my_ctx = lane < nrows ? min((int)ctx_lens[row0 + lane], max_ctx) : 0;
+  int lmax = my_ctx;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) lmax = max(lmax, __shfl_xor(lmax, o, 64));
+  lmax = __builtin_amdgcn_readfirstlane(lmax);
+  if (lmax <= 0) return;
   const int32_t* bt = block_table + (size_t)r * max_blocks;
 
-  if (tid < QB) lens[tid] = tid < nrows ? min((int)ctx_lens[row0 + tid], max_ctx) : 0;
-  if (tid < (t_end - t_begin + APS - 1) / APS) pgs[tid] = bt[t_begin / APS + tid];
+  if (tid < QB) lens[tid] = my_ctx;
 
   // this lane's column in the score layout, and its q as the B operand
   const int cl = lane & 15;
@@ -297,6 +305,8 @@ __global__ __launch_bounds__(256) void attn_prefill_chunk_kernel(
   __syncthreads();
   const int my_len = lens[col / G];
 
+  // K/V tile loader: chunk ci = tid + 256 i is token 16 i + tid/16 of the
+  // tile, so every lane needs the same four page ids (scalar loads)
   u32x4_t kr[4], vr[4];
   auto load_tile = [&](int t0, int nt) {
 #pragma unroll
@@ -306,9 +316,9 @@ __global__ __launch_bounds__(256) void attn_prefill_chunk_kernel(
       const int dc = ci & 15;
       kr[i] = u32x4_t{0u, 0u, 0u, 0u};
       vr[i] = u32x4_t{0u, 0u, 0u, 0u};
+      const long long page = 16 * i < nt ? bt[t0 / APS + i] : -1;
       if (tt < nt) {
         const int t = t0 + tt;
-        const long long page = pgs[(t - t_begin) / APS];
         if (page >= 0 && page < num_pages) {
           const size_t kofs = (((size_t)page * 2 + 0) * Hkv + hk) * (APS * AD) + (t % APS) * AD + dc * 8;
           const size_t vofs = kofs + (size_t)Hkv * APS * AD;
@@ -339,15 +349,24 @@ __global__ __launch_bounds__(256) void attn_prefill_chunk_kernel(
   const uint32_t* vcol = (const uint32_t*)vs + lane;
   const float* pwv = &pw[wave][0][0];
 
-  load_tile(t_begin, min(ATILE, t_end - t_begin));
-  for (int t0 = t_begin; t0 < t_end; t0 += ATILE) {
-    const int nt = min(ATILE, t_end - t0);
+  load_tile(0, min(ATILE, lmax));
+  for (int t0 = 0; t0 < lmax; t0 += ATILE) {
+    const int nt = min(ATILE, lmax - t0);  // tiles never straddle a chunk
     __syncthreads();  // previous tile fully consumed
     store_tile();
     __syncthreads();
     const int t1 = t0 + ATILE;
-    if (t1 < t_end) load_tile(t1, min(ATILE, t_end - t1));
+    if (t1 < lmax) load_tile(t1, min(ATILE, lmax - t1));
     if (!wave_live) continue;
+    if (t0 % ACHUNK == 0) {  // a chunk starts: fresh online-softmax state
+      m_c = -INFINITY;
+      l_c = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        a0[j] = 0.0f;
+        a1[j] = 0.0f;
+      }
+    }
 
     // scores S^T = K Q^T for the tile's 64 tokens x the wave's 16 columns
     const int nt_c = min(nt, my_len - t0);  // this column's tokens in the tile
@@ -410,19 +429,19 @@ __global__ __launch_bounds__(256) void attn_prefill_chunk_kernel(
 
     // all 16 columns, tokens [0, nmin), in token order
     int i = 0;
-    for (; i + 4 <= nmin; i += 4) {
-      uint32_t v2[4];
-      float pl[4];
-      f32x4_t p[4][4];
+    for (; i + PU <= nmin; i += PU) {
+      uint32_t v2[PU];
+      float pl[PU];
+      f32x4_t p[PU][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < PU; ++u) {
         v2[u] = vcol[(i + u) * (AD / 2)];
         pl[u] = pwv[(i + u) * 16 + cl];
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) p[u][qd] = *(const f32x4_t*)(pwv + (i + u) * 16 + 4 * qd);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < PU; ++u) {
         l_c = l_c + pl[u];
         const float lo = bf16_lo(v2[u]), hi = bf16_hi(v2[u]);
 #pragma unroll
@@ -462,31 +481,83 @@ __global__ __launch_bounds__(256) void attn_prefill_chunk_kernel(
         }
       }
     }
-  }
 
-  // partials of the rows whose context reaches this chunk: [row][h][c][...]
-  if (!wave_live) return;
+    // the chunk ends: partials of the rows whose context reaches it,
+    // [row][h][chunk][m, l, -, -, acc].  Column j of the wave is row
+    // 16w/G + j/G, head j%G; the strides pass through an empty asm so that
+    // the sixteen addresses are formed here rather than held across the loop.
+    if (t1 % ACHUNK == 0 || t1 >= lmax) {
+      const int c = t0 / ACHUNK;
+      int hs = nc_stride * APART;
+      asm volatile("" : "+s"(hs));
+      float* pbase = part + ((size_t)(row0 + 16 * wave / G) * Hq + hk * G) * hs + (size_t)c * APART;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int cj = 16 * wave + j;
-    const int rr = cj / G;
-    if (rr < nrows && lens[rr] > t_begin) {
-      float* pp = part + (((size_t)(row0 + rr) * Hq + hk * G + cj % G) * nc_stride + c) * APART;
-      if (lane == j) {
-        pp[0] = m_c;
-        pp[1] = l_c;
+      for (int j = 0; j < 16; ++j) {
+        if (__builtin_amdgcn_readlane(my_len, j) > c * ACHUNK) {
+          float* pp = pbase + (size_t)((j / G) * Hq + j % G) * hs;
+          if (lane == j) {
+            pp[0] = m_c;
+            pp[1] = l_c;
+          }
+          pp[4 + 2 * lane] = a0[j];
+          pp[5 + 2 * lane] = a1[j];
+        }
       }
-      pp[4 + 2 * lane] = a0[j];
-      pp[5 + 2 * lane] = a1[j];
     }
   }
-}
 
+  // The combine, as the combine kernel does it, for the wave's columns: the
+  // workgroup has written every chunk partial of its rows.  M* = max m_c,
+  // w_c = exp(m_c - M*), L and O folded in chunk order, out = bf16(O / L).
+  if (!wave_live) return;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  int hs = nc_stride * APART;
+  asm volatile("" : "+s"(hs));
+  const float* pbase = part + ((size_t)(row0 + 16 * wave / G) * Hq + hk * G) * hs;
+  uint16_t* obase = out + ((size_t)(row0 + 16 * wave / G) * Hq + hk * G) * AD + 2 * lane;
+  for (int j = 0; j < 16; ++j) {
+    if (16 * wave + j >= nrows * G) break;
+    const int L = __builtin_amdgcn_readlane(my_len, j);
+    uint32_t* o = (uint32_t*)(obase + (size_t)((j / G) * Hq + j % G) * AD);
+    if (L <= 0) {
+      *o = 0u;
+      continue;
+    }
+    const int nc = min((L + ACHUNK - 1) / ACHUNK, ACOMB_MAXC);
+    const float* pp = pbase + (size_t)((j / G) * Hq + j % G) * hs;
+    float mx = -INFINITY;
+    for (int cc = lane; cc < nc; cc += 64) mx = fmaxf(mx, pp[(size_t)cc * APART]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    float ls = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int c0 = 0; c0 < nc; c0 += 8) {
+      float mv[8], lv[8], v0[8], v1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float* pc = pp + (size_t)min(c0 + u, nc - 1) * APART;
+        mv[u] = pc[0];
+        lv[u] = pc[1];
+        v0[u] = pc[4 + 2 * lane];
+        v1[u] = pc[5 + 2 * lane];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c0 + u < nc) {
+          const float w = __expf(mv[u] - mx);
+          ls = __fmaf_rn(lv[u], w, ls);
+          o0 = __fmaf_rn(v0[u], w, o0);
+          o1 = __fmaf_rn(v1[u], w, o1);
+        }
+      }
+    }
+    *o = (uint32_t)f32_to_bf16_bits(o0 / ls) | ((uint32_t)f32_to_bf16_bits(o1 / ls) << 16);
+  }
+}
 // grid = (num_q_heads, batch), block = 128 (one lane per dim).
 // The chunk maxima and weights are computed by all lanes in parallel (the
 // maximum does not depend on order); the two sums then run in chunk order,
 // with the partials of 32 chunks fetched before each stretch of the chain.
-static constexpr int ACOMB_MAXC = 1024;  // chunks per request the combine handles
 
 __global__ __launch_bounds__(128) void attn_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ ctx_lens,
@@ -611,15 +682,14 @@ int launch_prefill_attn(const uint16_t* q, const uint16_t* kv, const int32_t* bl
   if (ws_bytes < attn_ws_bytes(d, false, 0)) return BI_ERR_WORKSPACE;
   const int qb = 64 / G;
   const long long row_blocks = (max_rows_per_request + qb - 1) / qb;
-  if (ncs > 65535 || d->num_kv_heads > 65535 || (long long)requests * row_blocks > 65535)
-    return BI_ERR_UNSUPPORTED;
+  const long long nwg = (long long)d->num_kv_heads * requests * row_blocks;
+  if (nwg > 0x7fffffffLL) return BI_ERR_UNSUPPORTED;
   float* part = (float*)ws;
-  dim3 grid((unsigned)ncs, (unsigned)d->num_kv_heads, (unsigned)(requests * row_blocks));
 #define BI_PREFILL_LAUNCH(GG)                                                                  \
-  hipLaunchKernelGGL(attn_prefill_chunk_kernel<GG>, grid, dim3(256), 0, stream, q, kv,       \
-                     block_table, row_start, ctx_lens, part, d->num_q_heads, d->num_kv_heads, \
-                     d->max_blocks_per_seq, (long long)d->num_pages, d->max_ctx_len, ncs,     \
-                     (int)row_blocks, d->batch, d->scale)
+  hipLaunchKernelGGL(attn_prefill_kernel<GG>, dim3((unsigned)nwg), dim3(256), 0, stream, q,   \
+                     kv, block_table, row_start, ctx_lens, part, out, d->num_q_heads,         \
+                     d->num_kv_heads, requests, d->max_blocks_per_seq, (long long)d->num_pages, \
+                     d->max_ctx_len, ncs, (int)row_blocks, d->batch, d->scale)
   switch (G) {
     case 1: BI_PREFILL_LAUNCH(1); break;
     case 2: BI_PREFILL_LAUNCH(2); break;
@@ -628,10 +698,6 @@ int launch_prefill_attn(const uint16_t* q, const uint16_t* kv, const int32_t* bl
     default: return BI_ERR_UNSUPPORTED;
   }
 #undef BI_PREFILL_LAUNCH
-  if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)d->num_q_heads, (unsigned)d->batch),
-                     dim3(128), 0, stream, part, ctx_lens, out, d->num_q_heads, d->max_ctx_len,
-                     ncs, ACHUNK, 0);
   return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 
