@@ -46,18 +46,24 @@ static constexpr int KB = 32;        // K per matrix-core op
 // ---------------------------------------------------------------------------
 // Skinny kernel (M <= 64, the decode regime: W streamed once, HBM bound)
 // ---------------------------------------------------------------------------
-// One workgroup of 512 lanes per (64-column tile, 512-row segment of K):
-// 128-byte rows of W, so every W line fetched is used whole.  The segment's
-// sum goes to the workspace and gemm_fold_kernel adds the segments in order.
-// The whole 64 KB W slab is requested at once (8 loads of 16 B per lane),
-// then the x slab (16 MT rows, padded: rows >= M read as zero through the
-// buffer range check).  Both sit in LDS with 16-byte chunks XOR-swizzled by
-// row, so the transpose reads of W (4 consecutive rows) and the A-operand
-// reads of x (16 rows, same chunk) hit distinct banks.  The 4 x MT
-// matrix-core chains (16-column group, 16-row sub-tile) are spread over the
-// waves; each runs the segment's 16 K-blocks in order from +0.
-static constexpr int SK_BN = 64;
-static constexpr int SK_ROWS = 512;  // = KC
+// One workgroup of 512 lanes per (BN-column tile, 512-row segment of K),
+// BN = 128: 256-byte pieces of W rows, which the memory system streams
+// faster than 128-byte ones.  The segment's sum goes to the workspace and
+// gemm_fold_kernel adds the segments in order.  The x slab (16 MT rows,
+// padded: rows >= M read as zero through the buffer range check) is
+// requested first, then the whole W slab (16 B per lane per load, held in
+// registers).  W passes through LDS a quarter at a time (128 rows): each
+// quarter is written as soon as its loads land and its four K-blocks run
+// while the later quarters are still in flight.  LDS holds 16-byte chunks
+// XOR-swizzled by row, so the transpose reads of W (4 consecutive rows) and
+// the A-operand reads of x (16 rows, same chunk) spread over the banks.  The
+// (BN/16) x MT matrix-core chains (16-column group, 16-row sub-tile) are
+// spread over the waves; each runs the segment's 16 K-blocks in order from +0.
+static constexpr int SK_BN = 128;
+static constexpr int SK_ROWS = 512;   // = KC
+static constexpr int SK_QROWS = 128;  // W rows per LDS quarter
+static constexpr int SK_WCH = SK_BN / 8;           // 16-B chunks per W row
+static constexpr int SK_WLD = SK_ROWS * SK_WCH / 512;  // W loads per lane (16)
 
 __device__ __forceinline__ int sk_phys(int row, int chunk) {  // W: element offset of a 16-B chunk
   return row * SK_BN + ((chunk ^ (row & 7)) << 3);
@@ -67,10 +73,10 @@ __device__ __forceinline__ int sk_xphys(int row, int chunk) {  // x: rows of 64 
 }
 
 template <int MT>  // 16-row sub-tiles of x: 1, 2 or 4
-__global__ __launch_bounds__(512) void gemm_skinny_kernel(
+__global__ __launch_bounds__(512, MT == 4 ? 2 : 4) void gemm_skinny_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ part,
     int M, int N, int K) {
-  __shared__ __attribute__((aligned(16))) uint16_t wl[SK_ROWS * SK_BN];
+  __shared__ __attribute__((aligned(16))) uint16_t wl[SK_QROWS * SK_BN];
   __shared__ __attribute__((aligned(16))) uint16_t xl[16 * MT * SK_ROWS];
 
   const int tid = threadIdx.x;
@@ -88,17 +94,6 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)((size_t)M * K * 2));
   const uint32_t row_bytes = (uint32_t)N * 2;
 
-  // W slab: chunk c = tid + 512 i is row c/8, 16-B chunk c%8.  Rows past K
-  // read as zero.
-  u32x4_t wreg[8];
-  {
-    uint32_t off = (uint32_t)(k0 + (tid >> 3)) * row_bytes + (uint32_t)(n0 + (tid & 7) * 8) * 2;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      wreg[i] = bufld128(wr, off);
-      off += 64 * row_bytes;
-    }
-  }
   // x slab: chunk c = tid + 512 i is row c/64, 16-B chunk c%64 of the
   // segment (k past K, within a row, is never multiplied: such K-blocks are
   // skipped below)
@@ -109,25 +104,32 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(
     const int r = c >> 6, ch = c & 63;
     xreg[i] = bufld128(xr, r < M ? (uint32_t)(r * K + k0 + ch * 8) * 2 : 0x80000000u);
   }
+  // W slab: chunk c = tid + 512 i is row c/16, 16-B chunk c%16; loads
+  // 4q .. 4q+3 are quarter q.  Rows past K read as zero.
+  constexpr int RPL = 512 / SK_WCH;  // rows per load (32)
+  constexpr int LPQ = SK_QROWS / RPL;  // loads per quarter (4)
+  u32x4_t wreg[SK_WLD];
+  {
+    uint32_t off = (uint32_t)(k0 + tid / SK_WCH) * row_bytes +
+                   (uint32_t)(n0 + (tid % SK_WCH) * 8) * 2;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + 512 * i;
-    *(u32x4_t*)&wl[sk_phys(c >> 3, c & 7)] = wreg[i];
+    for (int i = 0; i < SK_WLD; ++i) {
+      wreg[i] = bufld128(wr, off);
+      off += RPL * row_bytes;
+    }
   }
 #pragma unroll
   for (int i = 0; i < 2 * MT; ++i) {
     const int c = tid + 512 * i;
     *(u32x4_t*)&xl[sk_xphys(c >> 6, c & 63)] = xreg[i];
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
-  // chains of this wave: column group wave%4, sub-tiles (wave/4)*SPW ..
-  constexpr int SPW = MT == 4 ? 2 : 1;        // sub-tiles per wave
-  if (MT == 1 && wave >= 4) return;
-  const int cg = wave & 3;
-  const int sub0 = (wave >> 2) * SPW;
+  // chains: (BN/16) column groups x MT sub-tiles over 8 waves; wave w takes
+  // column group w % CG and sub-tiles (w / CG) * SPW ..
+  constexpr int CG = SK_BN / 16;                 // 8
+  constexpr int SPW = MT * CG / 8;               // sub-tiles per wave: MT
+  const int cg = wave % CG;
+  const int sub0 = (wave / CG) * SPW;
   const int nkb = min(SK_ROWS, K - k0) / KB;
   const int chunk = 2 * cg + (tr_c >> 1);
   const int sub = (tr_c & 1) * 4;
@@ -135,20 +137,40 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(
 #pragma unroll
   for (int i = 0; i < SPW; ++i) a[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kb = 0; kb < 16; ++kb) {
-    if (kb < nkb) {
-      const int r0 = kb * KB + 8 * g + tr_r;
-      const u32x2_t b0 = lds_read_tr16(&wl[sk_phys(r0, chunk) + sub]);
-      const u32x2_t b1 = lds_read_tr16(&wl[sk_phys(r0 + 4, chunk) + sub]);
-      const u32x4_t bf = u32x4_t{b0.x, b0.y, b1.x, b1.y};
+  for (int q = 0; q < 4; ++q) {
+    if (q > 0) {  // every wave is done reading the previous quarter
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
 #pragma unroll
-      for (int i = 0; i < SPW; ++i) {
-        const u32x4_t af = *(const u32x4_t*)&xl[sk_xphys((sub0 + i) * 16 + arow, kb * 4 + g)];
-        a[i] = mfma16x16x32(af, bf, a[i]);
+    for (int h = 0; h < LPQ; ++h) {
+      const int c = tid + 512 * h;  // row c/16 of the quarter, chunk c%16
+      *(u32x4_t*)&wl[sk_phys(c / SK_WCH, c % SK_WCH)] = wreg[LPQ * q + h];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kb = 4 * q + j;
+      if (kb < nkb) {
+        const int r0 = j * KB + 8 * g + tr_r;
+        const u32x2_t b0 = lds_read_tr16(&wl[sk_phys(r0, chunk) + sub]);
+        const u32x2_t b1 = lds_read_tr16(&wl[sk_phys(r0 + 4, chunk) + sub]);
+        const u32x4_t bf = u32x4_t{b0.x, b0.y, b1.x, b1.y};
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+          const u32x4_t af = *(const u32x4_t*)&xl[sk_xphys((sub0 + i) * 16 + arow, kb * 4 + g)];
+          a[i] = mfma16x16x32(af, bf, a[i]);
+        }
       }
     }
   }
+  // N is a multiple of 64, not always of 128: the last tile's upper half
+  // (columns >= N, loaded from the next row or as zeros) is never stored
   const int col = n0 + 16 * cg + arow;
+  if (n0 + 16 * cg >= N) return;
 #pragma unroll
   for (int i = 0; i < SPW; ++i)
 #pragma unroll
@@ -472,7 +494,7 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
   if (S > 65535) return BI_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < (size_t)S * (size_t)M * (size_t)N * sizeof(float)) return BI_ERR_WORKSPACE;
   float* part = (float*)ws;
-  const dim3 grid((unsigned)(N / SK_BN), (unsigned)S);
+  const dim3 grid((unsigned)ceil_div(N, SK_BN), (unsigned)S);
   if (M <= 16)
     hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(512), 0, stream, x, W, part, (int)M,
                        (int)N, (int)K);
