@@ -305,6 +305,7 @@ def main():
         extras["mismatches_m1_vs_batch"] = mism
         extras["rmsnorm"] = bench_rmsnorm(torch, bi, synth, dev, args)
         extras["attention"] = bench_attn(torch, bi, synth, dev, args)
+        extras["tp8_shard"] = bench_tp8(torch, bi, synth, dev, args)
         extras["prefill_attention"] = bench_prefill_attn(torch, bi, synth, dev, args)
         extras["verify"] = bench_verify(torch, bi, synth, dev, args)
         result["extras"] = extras
@@ -432,6 +433,43 @@ def bench_prefill_attn(torch, bi, synth, dev, args):
     same = bool(torch.equal(outs["prefill"].view(torch.int16), outs["decode"].view(torch.int16)))
     return {"rows": M, "prompt_lens": [int(x) for x in lens], "prefill_us": res["prefill"],
             "decode_path_us": res["decode"], "bitwise_equal": same}
+
+
+def bench_tp8(torch, bi, synth, dev, args):
+    """One rank's share of the four linears under 8-way tensor parallelism
+    (Megatron layout): qkv and gate_up column-parallel (N = 768, 3584), o
+    and down row-parallel (K = 512; 14336 split on 512-row segments as
+    2048 / 1536), whose segment sums are gathered across ranks and folded.
+    Times each rank-local call at M = 16 and 2048, plus the fold of all
+    segments that follows the gather; reports the bytes each rank sends."""
+    out = {}
+    for M in (16, 2048):
+        row = {}
+        x = {K: synth.bf16_normal((M, K), seed=K, device=dev) for K in (4096, 512, 2048, 1536)}
+        cases = [("qkv", "col", 4096, 768), ("gate_up", "col", 4096, 3584),
+                 ("o", "row", 512, 4096), ("down_4seg", "row", 2048, 4096),
+                 ("down_3seg", "row", 1536, 4096)]
+        for name, kind, K, N in cases:
+            ws = [synth.bf16_normal((K, N), seed=100 + i, std=0.02, device=dev) for i in range(4)]
+            if kind == "col":
+                o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                calls = [(x[K], ws[i % 4], o) for i in range(8)]
+                us = graph_time_us(torch, bi.gemm, calls)
+                row[name] = {"K": K, "N": N, "us": us}
+            else:
+                S = (K + 511) // 512
+                part = torch.empty((S, M, N), dtype=torch.float32, device=dev)
+                calls = [(x[K], ws[i % 4], part) for i in range(8)]
+                us = graph_time_us(torch, lambda a, b, out: bi.gemm_segments(a, b, out), calls)
+                row[name] = {"K": K, "N": N, "us": us, "segments": S,
+                             "gather_bytes_sent": S * M * N * 4}
+        for name, S in (("o", 8), ("down", 28)):
+            part = torch.zeros((S, M, 4096), dtype=torch.float32, device=dev)
+            y = torch.empty((M, 4096), dtype=torch.bfloat16, device=dev)
+            row[f"fold_{name}_{S}seg"] = {"us": graph_time_us(
+                torch, lambda p, out: bi.gemm_fold(p, out), [(part, y)] * 8)}
+        out[str(M)] = row
+    return out
 
 
 def bench_attn(torch, bi, synth, dev, args):

@@ -109,6 +109,30 @@ int bi_gemm_fast(const bi_bf16 *x, const bi_bf16 *W, bi_bf16 *y,
                  void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * The two halves of bi_gemm's schedule, for a row-parallel (K-sharded)
+ * GEMM across ranks: the Article's section 4 design of fixed segments whose
+ * sums are combined in a fixed second stage, with the second stage placed
+ * after the exchange.  Each rank computes its shard's segment sums; the
+ * ranks gather every rank's segments in rank order (an all-gather, whose
+ * result does not depend on message size or rank count, unlike a ring or
+ * tree all-reduce); each then folds all of them.  When every shard but the
+ * last is a multiple of 512 rows of K, the folded y is bitwise bi_gemm's
+ * on the unsharded x and W, for any number of ranks.
+ *
+ * bi_gemm_segments: part[s][m][n] (fp32, [ceil(K/512)][M][N], caller
+ *   owned, 16-byte aligned) = sum over k in [512 s, min(512 s + 512, K)) of
+ *   x[m][k] W[k][n], accumulated from +0 in bi_gemm's order.  x, W as for
+ *   bi_gemm (same requirements); no workspace.
+ * bi_gemm_fold: y[m][n] = bf16(((part[0] + part[1]) + ...) + part[S-1]),
+ *   fp32 adds in index order, round to nearest even; part as above with S
+ *   segments, M <= 65535, N % 64 == 0, 16-byte aligned pointers.
+ * ---------------------------------------------------------------------- */
+int bi_gemm_segments(const bi_bf16 *x, const bi_bf16 *W, float *part,
+                     int64_t M, int64_t N, int64_t K, void *stream);
+int bi_gemm_fold(const float *part, bi_bf16 *y, int64_t M, int64_t N,
+                 int64_t S, void *stream);
+
+/* ------------------------------------------------------------------------
  * RMSNorm:  y[m,h] = bf16_rne( (x[m,h] * r_m) * g[h] ),
  *           r_m = 1 / sqrt( (sum_h x[m,h]^2) / H + eps ),  fp32 throughout.
  *

@@ -27,4 +27,6 @@ from ._lib import (  # noqa: F401
     silu_mul,
     add,
     paged_prefill_attn,
+    gemm_segments,
+    gemm_fold,
 )

@@ -37,7 +37,8 @@ EXPORTS = ("bi_version", "bi_status_string", "bi_gemm_workspace_bytes", "bi_gemm
            "bi_gemm_fast_workspace_bytes", "bi_gemm_fast", "bi_rmsnorm", "bi_rmsnorm_fast",
            "bi_attn_workspace_bytes", "bi_paged_decode_attn", "bi_attn_fast_workspace_bytes",
            "bi_paged_decode_attn_fast", "bi_embed", "bi_rope_table", "bi_rope", "bi_kv_append",
-           "bi_silu_mul", "bi_add", "bi_paged_prefill_attn")
+           "bi_silu_mul", "bi_add", "bi_paged_prefill_attn",
+           "bi_gemm_segments", "bi_gemm_fold")
 
 _lock = threading.Lock()
 _lib = None
@@ -85,6 +86,8 @@ def load(path: str | None = None):
             "bi_add": [vp, vp, vp, i64, vp],
             "bi_paged_prefill_attn": [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AttnDesc), i32, i32,
                                       vp, sz, vp],
+            "bi_gemm_segments": [vp, vp, vp, i64, i64, i64, vp],
+            "bi_gemm_fold": [vp, vp, i64, i64, i64, vp],
         }
         for f, a in sigs.items():
             getattr(lib, f).restype = ctypes.c_int
@@ -403,3 +406,39 @@ def paged_prefill_attn(q, kv_pages, block_table, row_start, ctx_lens, max_rows_p
                                    _stream(q.device))
     _raise(st, "bi_paged_prefill_attn")
     return out
+
+
+def gemm_segments(x, W, part=None):
+    """Segment sums of x @ W: [ceil(K/512), M, N] float32, segment s over K
+    rows [512 s, 512 s + 512), each from +0 (the local half of a K-sharded
+    GEMM)."""
+    lib = load()
+    _check_bf16(x, "x", 2)
+    _check_bf16(W, "W", 2)
+    M, K = x.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError("x and W disagree on K")
+    S = (K + 511) // 512
+    if part is None:
+        part = torch.empty((S, M, N), dtype=torch.float32, device=x.device)
+    if tuple(part.shape) != (S, M, N) or part.dtype != torch.float32 or not part.is_contiguous():
+        raise ValueError("part must be contiguous float32 [ceil(K/512), M, N]")
+    st = lib.bi_gemm_segments(x.data_ptr(), W.data_ptr(), part.data_ptr(), M, N, K,
+                              _stream(x.device))
+    _raise(st, "bi_gemm_segments")
+    return part
+
+
+def gemm_fold(part, y=None):
+    """bf16 of the left-to-right fp32 sum of part's segments ([S, M, N])."""
+    lib = load()
+    if part.dtype != torch.float32 or part.dim() != 3 or not part.is_contiguous():
+        raise ValueError("part must be contiguous float32 [S, M, N]")
+    S, M, N = part.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=part.device)
+    _check_bf16(y, "y", 2)
+    st = lib.bi_gemm_fold(part.data_ptr(), y.data_ptr(), M, N, S, _stream(part.device))
+    _raise(st, "bi_gemm_fold")
+    return y

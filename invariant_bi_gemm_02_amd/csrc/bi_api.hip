@@ -133,6 +133,24 @@ int bi_gemm_fast(const bi_bf16* x, const bi_bf16* W, bi_bf16* y, int64_t M, int6
   return gemm_entry(x, W, y, M, N, K, ws, ws_bytes, stream, true);
 }
 
+int bi_gemm_segments(const bi_bf16* x, const bi_bf16* W, float* part, int64_t M, int64_t N,
+                     int64_t K, void* stream) {
+  int st = check_gemm(x, W, part, M, N, K);
+  if (st != BI_OK) return st;
+  const int64_t S = (K + 511) / 512;
+  if (S * M * N >= kMaxElems * 64) return BI_ERR_SHAPE;
+  return bi::launch_gemm_segments(x, W, part, M, N, K, (hipStream_t)stream);
+}
+
+int bi_gemm_fold(const float* part, bi_bf16* y, int64_t M, int64_t N, int64_t S, void* stream) {
+  if (!part || !y) return BI_ERR_NULL;
+  if (M <= 0 || N <= 0 || S <= 0 || M > 65535 || S > 65535 || N >= kMaxElems ||
+      M * N >= kMaxElems)
+    return BI_ERR_SHAPE;
+  if (N % 64 != 0 || !aligned16(part) || !aligned16(y)) return BI_ERR_UNSUPPORTED;
+  return bi::launch_gemm_fold(part, y, M, N, S, (hipStream_t)stream);
+}
+
 int bi_rmsnorm(const bi_bf16* x, const bi_bf16* g, bi_bf16* y, int64_t M, int64_t H, float eps,
                void* stream) {
   int st = check_rms(x, g, y, M, H);

@@ -510,4 +510,40 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
   return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 
+// Segment sums only ([S][M][N] fp32, segment s over K rows [512 s, 512 s +
+// 512) from +0): the local half of a row-parallel (K-sharded) GEMM, whose
+// ranks gather every rank's segments in rank order and fold them with
+// launch_gemm_fold, reproducing the unsharded bits.
+int launch_gemm_segments(const uint16_t* x, const uint16_t* W, float* part, int64_t M, int64_t N,
+                         int64_t K, hipStream_t stream) {
+  const int64_t S = ceil_div(K, BI_KC);
+  if (S > 65535) return BI_ERR_UNSUPPORTED;
+  if (M <= SKINNY_MAX_M) {
+    const dim3 grid((unsigned)ceil_div(N, SK_BN), (unsigned)S);
+    if (M <= 16)
+      hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(512), 0, stream, x, W, part, (int)M,
+                         (int)N, (int)K);
+    else if (M <= 32)
+      hipLaunchKernelGGL(gemm_skinny_kernel<2>, grid, dim3(512), 0, stream, x, W, part, (int)M,
+                         (int)N, (int)K);
+    else
+      hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(512), 0, stream, x, W, part, (int)M,
+                         (int)N, (int)K);
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+  }
+  const int64_t tm = ceil_div(M, TILE_BM), tn = ceil_div(N, TL_BN);
+  const int remap = (tn % 8 == 0) ? 2 : ((tm * tn) % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((gemm_tile_kernel<false, true>), dim3((unsigned)(tm * tn), (unsigned)S),
+                     dim3(512), 0, stream, x, W, (uint16_t*)nullptr, (int)M, (int)N, (int)K, BI_KC,
+                     (int)tm, (int)tn, remap, part);
+  return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+int launch_gemm_fold(const float* part, uint16_t* y, int64_t M, int64_t N, int64_t S,
+                     hipStream_t stream) {
+  hipLaunchKernelGGL(gemm_fold_kernel, dim3((unsigned)ceil_div(N, 256), (unsigned)M), dim3(64), 0,
+                     stream, part, y, (int)M, (int)N, (int)S);
+  return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
 }  // namespace bi

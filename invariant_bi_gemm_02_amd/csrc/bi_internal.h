@@ -26,6 +26,10 @@ int launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* block_tabl
                 const int32_t* ctx_lens, uint16_t* out, const bi_attn_desc* d, void* ws,
                 size_t ws_bytes, hipStream_t stream, bool fast, int num_cus);
 
+int launch_gemm_segments(const uint16_t* x, const uint16_t* W, float* part, int64_t M, int64_t N,
+                         int64_t K, hipStream_t stream);
+int launch_gemm_fold(const float* part, uint16_t* y, int64_t M, int64_t N, int64_t S,
+                     hipStream_t stream);
 int launch_prefill_attn(const uint16_t* q, const uint16_t* kv, const int32_t* block_table,
                         const int32_t* row_start, const int32_t* ctx_lens, uint16_t* out,
                         const bi_attn_desc* d, int requests, int max_rows_per_request, void* ws,

@@ -70,6 +70,18 @@ def test_gemm_argument_checks(lib):
     assert lib.bi_gemm_workspace_bytes(2048, 4096, 4096) == 0
 
 
+def test_segment_and_fold_argument_checks(lib):
+    ok = 0x1000
+    assert lib.bi_gemm_segments(None, P(ok), P(ok), 1, 64, 512, None) == -1
+    assert lib.bi_gemm_segments(P(ok), P(ok), P(ok), 1, 64, 33, None) == -3   # K % 32
+    assert lib.bi_gemm_segments(P(ok), P(ok), P(ok), 0, 64, 512, None) == -2
+    assert lib.bi_gemm_fold(None, P(ok), 1, 64, 1, None) == -1
+    assert lib.bi_gemm_fold(P(ok), P(ok), 1, 64, 0, None) == -2
+    assert lib.bi_gemm_fold(P(ok), P(ok), 70000, 64, 1, None) == -2           # M > 65535
+    assert lib.bi_gemm_fold(P(ok), P(ok), 1, 96, 1, None) == -3               # N % 64
+    assert lib.bi_gemm_fold(P(ok + 4), P(ok), 1, 64, 1, None) == -3           # alignment
+
+
 def test_workspace_size_counts_segments(lib):
     a = lib.bi_gemm_workspace_bytes(40, 4096, 4096)
     b = lib.bi_gemm_workspace_bytes(40, 4096, 14336)
