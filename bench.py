@@ -382,11 +382,44 @@ def bench_verify(torch, bi, synth, dev, args):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    mism = 0
+    # per-request sampling of the window (seed per request, step = the
+    # position sampled) and the commit-or-rollback step, with candidates that
+    # diverge from the recompute at a drawn point of each window
+    up = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)
+    order = np.lexsort((pos, rid))          # windows grouped by request, in position order
+    inv = np.empty_like(order)
+    inv[order] = np.arange(len(order))
+    g_logits = grouped[torch.from_numpy(order).to(dev)].contiguous()
+    seeds = up(1000003 * rid[order] + 17, np.uint64)
+    steps = up(pos[order] + 1, np.uint64)
+    temps = up(np.full(len(win), 0.8), np.float32)
+    row_start = up(np.concatenate([[0], np.cumsum(sizes)]), np.int32)
+    ver = bi.sample(g_logits, seeds, steps, temps)
+    cand = ver.clone()
+    drng = np.random.default_rng(16)
+    for r, (a, b) in enumerate(zip(np.concatenate([[0], np.cumsum(sizes)])[:-1], np.cumsum(sizes))):
+        k = int(drng.integers(a, b + 1))
+        if k < b:
+            cand[k] = (cand[k] + 1) % cfg.vocab
+    commit = up(np.array(req.prompt_lens), np.int32)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        ver = bi.sample(g_logits, seeds, steps, temps, tokens=ver)
+        bi.verify_commit(cand, ver, row_start, commit.clone())
+    e1.record()
+    torch.cuda.synchronize()
+    ms_commit = e0.elapsed_time(e1) / reps
+    acc, fix = bi.verify_commit(cand, ver, row_start, commit)
+    mism, tok_mism = 0, 0
     for r in range(len(sizes)):
         sel = np.nonzero(rid == r)[0]
         alone = dec.forward(*req.rows(rid[sel], pos[sel], tok[sel]))
         mism += int((alone.view(torch.int16) != grouped[sel].view(torch.int16)).sum())
+        t_alone = bi.sample(alone.contiguous(), up(1000003 * rid[sel] + 17, np.uint64),
+                            up(pos[sel] + 1, np.uint64), up(np.full(len(sel), 0.8), np.float32))
+        t_grp = ver[torch.from_numpy(inv[sel]).to(dev)]
+        tok_mism += int((t_alone != t_grp).sum())
     out = {"config": "Llama-3-8B shape, 32 layers, random init, vocab 128256",
            "requests": len(sizes), "window_tokens": int(len(win)), "group_sizes": sizes,
            "prompt_lens": [int(x) for x in lens],
@@ -394,7 +427,11 @@ def bench_verify(torch, bi, synth, dev, args):
            "prefill_tokens_per_s": float(np.sum(lens)) / (ms_prefill * 1e-3),
            "logit_mismatches_prefill_vs_last_token_alone": pre_mism,
            "ms_per_verify": ms,
-           "tokens_per_s": len(win) / (ms * 1e-3), "logit_mismatches_grouped_vs_alone": mism}
+           "tokens_per_s": len(win) / (ms * 1e-3), "logit_mismatches_grouped_vs_alone": mism,
+           "ms_sample_and_commit": ms_commit,
+           "sampled_token_mismatches_grouped_vs_alone": tok_mism,
+           "accepted_per_request": [int(v) for v in acc.cpu()],
+           "committed_lens": [int(v) for v in commit.cpu()]}
     del dec, w, grouped
     torch.cuda.empty_cache()
     return out

@@ -240,6 +240,46 @@ int bi_paged_prefill_attn(const bi_bf16 *q, const bi_bf16 *kv_pages,
                           size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Per-request sampling (the Determinism article, section 6, item 3: a
+ * counter-based generator of the Philox family keyed by request and step
+ * instead of a shared random stream).  Row m's token depends only on its
+ * logits row, seeds[m] and steps[m]:
+ *   Philox4x64-10 (Salmon et al., SC 2011) with key (seeds[m], 0) and
+ *   counter (v / 4, steps[m], 0, 0); vocabulary entry v takes word v % 4;
+ *   u = ((word >> 41) + 1/2) * 2^-23 (fp32, in (0, 1));
+ *   temperature[m] > 0: Gumbel-max, score = l / T + (-log(-log u)) in fp32;
+ *   temperature[m] <= 0 or NaN: greedy, score = l;
+ *   tokens[m] = the first index of the largest score (NaN counts as -inf).
+ * logits [M, V] bf16; seeds, steps [M] uint64; temperature [M] fp32;
+ * tokens [M] int32 out; all device memory.  V < 2^31.
+ * ---------------------------------------------------------------------- */
+int bi_sample(const bi_bf16 *logits, int64_t M, int64_t V,
+              const uint64_t *seeds, const uint64_t *steps,
+              const float *temperature, int32_t *tokens, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Commit or rollback after a grouped verification pass (the LLM-42 digest,
+ * method: the prefix the fixed-shape recompute confirms is committed; at
+ * the first mismatch the later candidates are discarded, their KV rolled
+ * back, and decoding resumes from the committed prefix).
+ * Request r's window is rows row_start[r] .. row_start[r+1]-1 (position
+ * order, clamped to [0, rows)); candidates[i] is the fast path's token for
+ * the position after row i, verified[i] the fixed-shape recompute's
+ * (bi_sample of that row's logits with the request's seed and step).
+ *   accepted[r]   = a, the number of leading windows rows that match;
+ *   commit_len[r] (in: committed tokens L) out: L + a + 1 if a < w (the
+ *                 recompute's token at the mismatch is committed), else
+ *                 L + w; the request's KV is valid for the first
+ *                 commit_len - 1 positions, later slots are overwritten;
+ *   fix_token[r]  = verified[row_start[r] + a] if a < w, else -1.
+ * All arrays int32 device memory; rows = length of candidates/verified.
+ * ---------------------------------------------------------------------- */
+int bi_verify_commit(const int32_t *candidates, const int32_t *verified,
+                     int32_t rows, const int32_t *row_start, int32_t requests,
+                     int32_t *accepted, int32_t *commit_len, int32_t *fix_token,
+                     void *stream);
+
+/* ------------------------------------------------------------------------
  * Element-wise steps of a Llama-style decoder layer built around the three
  * calls above.  [LLM-42] problem statement: a token's logits must come out
  * the same whether it is verified alone or grouped with other requests, so

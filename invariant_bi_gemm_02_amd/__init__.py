@@ -29,4 +29,6 @@ from ._lib import (  # noqa: F401
     paged_prefill_attn,
     gemm_segments,
     gemm_fold,
+    sample,
+    verify_commit,
 )

@@ -38,7 +38,7 @@ EXPORTS = ("bi_version", "bi_status_string", "bi_gemm_workspace_bytes", "bi_gemm
            "bi_attn_workspace_bytes", "bi_paged_decode_attn", "bi_attn_fast_workspace_bytes",
            "bi_paged_decode_attn_fast", "bi_embed", "bi_rope_table", "bi_rope", "bi_kv_append",
            "bi_silu_mul", "bi_add", "bi_paged_prefill_attn",
-           "bi_gemm_segments", "bi_gemm_fold")
+           "bi_gemm_segments", "bi_gemm_fold", "bi_sample", "bi_verify_commit")
 
 _lock = threading.Lock()
 _lib = None
@@ -87,6 +87,8 @@ def load(path: str | None = None):
             "bi_paged_prefill_attn": [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AttnDesc), i32, i32,
                                       vp, sz, vp],
             "bi_gemm_segments": [vp, vp, vp, i64, i64, i64, vp],
+            "bi_sample": [vp, i64, i64, vp, vp, vp, vp, vp],
+            "bi_verify_commit": [vp, vp, i32, vp, i32, vp, vp, vp, vp],
             "bi_gemm_fold": [vp, vp, i64, i64, i64, vp],
         }
         for f, a in sigs.items():
@@ -442,3 +444,40 @@ def gemm_fold(part, y=None):
     st = lib.bi_gemm_fold(part.data_ptr(), y.data_ptr(), M, N, S, _stream(part.device))
     _raise(st, "bi_gemm_fold")
     return y
+
+
+def sample(logits, seeds, steps, temperature, tokens=None):
+    """Per-row token of logits [M, V] (bf16): Gumbel-max with Philox noise
+    keyed by (seeds[m], steps[m]) at temperature[m] > 0, else argmax."""
+    lib = load()
+    _check_bf16(logits, "logits", 2)
+    M, V = logits.shape
+    for t, n, dt in ((seeds, "seeds", torch.uint64), (steps, "steps", torch.uint64),
+                     (temperature, "temperature", torch.float32)):
+        if t.dtype != dt or t.shape != (M,) or not t.is_contiguous() or t.device != logits.device:
+            raise ValueError(f"{n} must be a contiguous {dt} [M] tensor on the logits' device")
+    if tokens is None:
+        tokens = torch.empty(M, dtype=torch.int32, device=logits.device)
+    st = lib.bi_sample(logits.data_ptr(), M, V, seeds.data_ptr(), steps.data_ptr(),
+                       temperature.data_ptr(), tokens.data_ptr(), _stream(logits.device))
+    _raise(st, "bi_sample")
+    return tokens
+
+
+def verify_commit(candidates, verified, row_start, commit_len):
+    """Commit-or-rollback of grouped verification windows; commit_len [R]
+    is updated in place.  Returns (accepted [R], fix_token [R])."""
+    lib = load()
+    for t, n in ((candidates, "candidates"), (verified, "verified"), (row_start, "row_start"),
+                 (commit_len, "commit_len")):
+        _check_i32(t, n)
+    R = row_start.shape[0] - 1
+    if commit_len.shape[0] != R or verified.shape != candidates.shape:
+        raise ValueError("commit_len must be [R] and verified match candidates")
+    acc = torch.empty(R, dtype=torch.int32, device=row_start.device)
+    fix = torch.empty(R, dtype=torch.int32, device=row_start.device)
+    st = lib.bi_verify_commit(candidates.data_ptr(), verified.data_ptr(), candidates.shape[0],
+                              row_start.data_ptr(), R, acc.data_ptr(), commit_len.data_ptr(),
+                              fix.data_ptr(), _stream(row_start.device))
+    _raise(st, "bi_verify_commit")
+    return acc, fix

@@ -151,6 +151,30 @@ int bi_gemm_fold(const float* part, bi_bf16* y, int64_t M, int64_t N, int64_t S,
   return bi::launch_gemm_fold(part, y, M, N, S, (hipStream_t)stream);
 }
 
+int bi_sample(const bi_bf16* logits, int64_t M, int64_t V, const uint64_t* seeds,
+              const uint64_t* steps, const float* temperature, int32_t* tokens, void* stream) {
+  if (!logits || !seeds || !steps || !temperature || !tokens) return BI_ERR_NULL;
+  if (M <= 0 || V <= 0 || M > 0x7fffffff || V >= kMaxElems || M * V >= kMaxElems * 64)
+    return BI_ERR_SHAPE;
+  if (((uintptr_t)logits & 1u) || ((uintptr_t)seeds & 7u) || ((uintptr_t)steps & 7u) ||
+      ((uintptr_t)temperature & 3u) || ((uintptr_t)tokens & 3u))
+    return BI_ERR_UNSUPPORTED;
+  return bi::launch_sample(logits, M, V, seeds, steps, temperature, tokens, (hipStream_t)stream);
+}
+
+int bi_verify_commit(const int32_t* candidates, const int32_t* verified, int32_t rows,
+                     const int32_t* row_start, int32_t requests, int32_t* accepted,
+                     int32_t* commit_len, int32_t* fix_token, void* stream) {
+  if (!candidates || !verified || !row_start || !accepted || !commit_len || !fix_token)
+    return BI_ERR_NULL;
+  if (rows < 0 || requests <= 0) return BI_ERR_SHAPE;
+  if (((uintptr_t)candidates | (uintptr_t)verified | (uintptr_t)row_start | (uintptr_t)accepted |
+       (uintptr_t)commit_len | (uintptr_t)fix_token) & 3u)
+    return BI_ERR_UNSUPPORTED;
+  return bi::launch_verify_commit(candidates, verified, row_start, requests, rows, accepted,
+                                  commit_len, fix_token, (hipStream_t)stream);
+}
+
 int bi_rmsnorm(const bi_bf16* x, const bi_bf16* g, bi_bf16* y, int64_t M, int64_t H, float eps,
                void* stream) {
   int st = check_rms(x, g, y, M, H);

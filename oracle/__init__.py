@@ -19,6 +19,12 @@ schedule oracle.  Parity status per function:
                      cases, page-layout invariance); the last bits of exp and
                      the association inside each 32-dim block of q.k are
                      unpinned (covered by the tolerance).
+* ``philox4x64``     pinned against numpy's Philox bit generator.
+* ``sample``         pinned (greedy = argmax with first-index ties, uniform
+                     range and moments, Gumbel-max frequencies against the
+                     softmax, temperature limits); its logarithms are the
+                     platform's, so near-ties are unpinned.
+* ``verify_commit``  pinned by worked cases of the commit-or-rollback rule.
 """
 from __future__ import annotations
 
@@ -30,7 +36,8 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "bi_oracle.c"), os.path.join(_HERE, "bi_oracle_layer.c")]
+_SRCS = [os.path.join(_HERE, "bi_oracle.c"), os.path.join(_HERE, "bi_oracle_layer.c"),
+         os.path.join(_HERE, "bi_oracle_sample.c")]
 _LIB = os.path.join(_HERE, "libbi_oracle.so")
 _CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
            "-shared", "-Wall", "-Wextra"]
@@ -76,10 +83,15 @@ def _load():
             lib.or_rope.argtypes = [p, p, p, i64, ci, ci, i64, p, p, i64]
             lib.or_silu_mul.argtypes = [p, p, i64, i64]
             lib.or_add.argtypes = [p, p, p, i64]
+            lib.or_philox4x64.argtypes = [p, p, p]
+            lib.or_philox4x64.restype = None
+            lib.or_sample_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64, i64]
+            lib.or_sample_uniform.restype = ctypes.c_float
+            lib.or_sample.argtypes = [p, i64, i64, p, p, p, p, p, p]
             for f in ("or_gemm", "or_gemm_exact", "or_gemm_absdot", "or_rmsnorm",
                       "or_rmsnorm_exact", "or_paged_decode_attn",
                       "or_paged_decode_attn_exact", "or_rope_table", "or_rope",
-                      "or_silu_mul", "or_add"):
+                      "or_silu_mul", "or_add", "or_sample"):
                 getattr(lib, f).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -261,3 +273,57 @@ def add(a, b):
     y = np.empty_like(a)
     _check(_load().or_add(_ptr(a), _ptr(b), _ptr(y), a.size), "add")
     return y
+
+
+def philox4x64(counter, key):
+    """Philox4x64-10 of one 4-word counter under a 2-word key (uint64)."""
+    c = np.ascontiguousarray(counter, dtype=np.uint64)
+    k = np.ascontiguousarray(key, dtype=np.uint64)
+    out = np.empty(4, dtype=np.uint64)
+    _load().or_philox4x64(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sample_uniform(seed: int, step: int, v: int) -> float:
+    """The fp32 uniform that vocabulary entry v draws at (seed, step)."""
+    return float(_load().or_sample_uniform(ctypes.c_uint64(seed), ctypes.c_uint64(step), v))
+
+
+def sample(logits, seeds, steps, temps, return_scores: bool = False):
+    """Per-row token: Gumbel-max over logits / T with Philox noise keyed by
+    (seed, step), or argmax where T <= 0; ties to the first index."""
+    logits = _u16(logits)
+    M, V = logits.shape
+    seeds = np.ascontiguousarray(seeds, dtype=np.uint64)
+    steps = np.ascontiguousarray(steps, dtype=np.uint64)
+    temps = np.ascontiguousarray(temps, dtype=np.float32)
+    tok = np.empty(M, dtype=np.int32)
+    best = np.empty(M, dtype=np.float32)
+    second = np.empty(M, dtype=np.float32)
+    _check(_load().or_sample(_ptr(logits), M, V, _ptr(seeds), _ptr(steps), _ptr(temps),
+                             _ptr(tok), _ptr(best), _ptr(second)), "sample")
+    return (tok, best, second) if return_scores else tok
+
+
+def verify_commit(candidates, verified, row_start, commit_len):
+    """Commit-or-rollback of grouped verification windows (LLM-42 digest,
+    method): request r's window is rows row_start[r] .. row_start[r+1]-1 in
+    position order; candidates[i] is the fast path's token for the position
+    after row i, verified[i] the fixed-shape recompute's token there.  The
+    leading matches are committed; at the first mismatch the recompute's
+    token is committed instead and every later candidate is dropped.
+    Returns (accepted, new commit length, correction token or -1)."""
+    rs = [int(v) for v in row_start]
+    acc, new_len, fix = [], [], []
+    for r in range(len(rs) - 1):
+        a, w = 0, rs[r + 1] - rs[r]
+        while a < w and int(candidates[rs[r] + a]) == int(verified[rs[r] + a]):
+            a += 1
+        acc.append(a)
+        if a < w:
+            new_len.append(int(commit_len[r]) + a + 1)
+            fix.append(int(verified[rs[r] + a]))
+        else:
+            new_len.append(int(commit_len[r]) + w)
+            fix.append(-1)
+    return (np.array(acc, np.int32), np.array(new_len, np.int32), np.array(fix, np.int32))

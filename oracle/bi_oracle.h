@@ -41,4 +41,11 @@ int or_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, int64_t M, int h
             int64_t max_pos);
 int or_silu_mul(const uint16_t *gu, uint16_t *y, int64_t M, int64_t F);
 int or_add(const uint16_t *a, const uint16_t *b, uint16_t *y, int64_t n);
+
+/* bi_oracle_sample.c: per-request counter-based sampling */
+void or_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]);
+float or_sample_uniform(uint64_t seed, uint64_t step, int64_t v);
+int or_sample(const uint16_t *logits, int64_t M, int64_t V, const uint64_t *seeds,
+              const uint64_t *steps, const float *temps, int32_t *tokens, float *best_score,
+              float *second_score);
 #endif

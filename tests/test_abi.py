@@ -82,6 +82,16 @@ def test_segment_and_fold_argument_checks(lib):
     assert lib.bi_gemm_fold(P(ok + 4), P(ok), 1, 64, 1, None) == -3           # alignment
 
 
+def test_sample_and_commit_argument_checks(lib):
+    ok = 0x1000
+    assert lib.bi_sample(None, 1, 10, P(ok), P(ok), P(ok), P(ok), None) == -1
+    assert lib.bi_sample(P(ok), 0, 10, P(ok), P(ok), P(ok), P(ok), None) == -2
+    assert lib.bi_sample(P(ok), 1, 10, P(ok + 4), P(ok), P(ok), P(ok), None) == -3  # seeds % 8
+    assert lib.bi_verify_commit(P(ok), None, 4, P(ok), 1, P(ok), P(ok), P(ok), None) == -1
+    assert lib.bi_verify_commit(P(ok), P(ok), 4, P(ok), 0, P(ok), P(ok), P(ok), None) == -2
+    assert lib.bi_verify_commit(P(ok), P(ok), 4, P(ok + 2), 1, P(ok), P(ok), P(ok), None) == -3
+
+
 def test_workspace_size_counts_segments(lib):
     a = lib.bi_gemm_workspace_bytes(40, 4096, 4096)
     b = lib.bi_gemm_workspace_bytes(40, 4096, 14336)
