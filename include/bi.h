@@ -314,7 +314,9 @@ int bi_rope_table(double theta, int32_t head_dim, int64_t max_pos,
  * elements (so a slice of a fused q|k|v row can be read in place).  out:
  * [M, heads, 128] bf16.  pos: [M] int32; positions outside [0, max_pos)
  * give zeros.  cos_t, sin_t: device copies of the bi_rope_table arrays.
- * Requirements: M, heads >= 1; head_dim == 128; x_row_stride >= heads*128. */
+ * Requirements: M, heads >= 1; head_dim == 128; x_row_stride >= heads*128
+ * and a multiple of 4; x and out 8-byte aligned; cos_t, sin_t 16-byte
+ * aligned. */
 int bi_rope(const bi_bf16 *x, int64_t x_row_stride, bi_bf16 *out,
             const int32_t *pos, const float *cos_t, const float *sin_t,
             int64_t M, int32_t heads, int32_t head_dim, int64_t max_pos,

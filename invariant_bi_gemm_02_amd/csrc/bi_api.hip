@@ -268,7 +268,8 @@ int bi_rope(const bi_bf16* x, int64_t x_row_stride, bi_bf16* out, const int32_t*
   if (M <= 0 || heads <= 0 || max_pos <= 0 || M >= kMaxElems || heads > 65535 ||
       x_row_stride < (int64_t)heads * 128 || M * x_row_stride >= kMaxElems)
     return BI_ERR_SHAPE;
-  if (head_dim != 128 || ((uintptr_t)x & 1u) || ((uintptr_t)out & 1u) || ((uintptr_t)pos & 3u))
+  if (head_dim != 128 || ((uintptr_t)x & 7u) || ((uintptr_t)out & 7u) || ((uintptr_t)pos & 3u) ||
+      (x_row_stride & 3) || !aligned16(cos_t) || !aligned16(sin_t))
     return BI_ERR_UNSUPPORTED;
   return bi::launch_rope(x, x_row_stride, out, pos, cos_t, sin_t, M, heads, max_pos,
                          (hipStream_t)stream);

@@ -39,35 +39,46 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// RoPE of `heads` head vectors of D = 128 per row.  grid = (M, heads),
-// block = 64: lane i owns the pair (i, i + 64).  x rows are x_stride elements
-// apart; out is [M, heads, D].  Positions outside [0, max_pos) give zeros.
-__global__ __launch_bounds__(64) void rope_kernel(const uint16_t* __restrict__ x,
-                                                  int64_t x_stride, uint16_t* __restrict__ out,
-                                                  const int32_t* __restrict__ pos,
-                                                  const float* __restrict__ cos_t,
-                                                  const float* __restrict__ sin_t, int heads,
-                                                  int64_t max_pos) {
+// RoPE of `heads` head vectors of D = 128 per row.  block = 256 lanes, 16
+// per head vector (16 heads per workgroup): lane i of a head owns the pairs
+// (4i .. 4i+3, 4i+64 .. 4i+67), read and written 8 bytes at a time.
+// grid = (M, ceil(heads / 16)).  x rows are x_stride elements apart; out is
+// [M, heads, D].  Positions outside [0, max_pos) give zeros.
+__global__ __launch_bounds__(256) void rope_kernel(const uint16_t* __restrict__ x,
+                                                   int64_t x_stride, uint16_t* __restrict__ out,
+                                                   const int32_t* __restrict__ pos,
+                                                   const float* __restrict__ cos_t,
+                                                   const float* __restrict__ sin_t, int heads,
+                                                   int64_t max_pos) {
   constexpr int D = 128, HALF = 64;
   const int64_t m = blockIdx.x;
-  const int h = blockIdx.y;
-  const int i = threadIdx.x;
+  const int h = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int i = (threadIdx.x & 15) * 4;
+  if (h >= heads) return;
   const int64_t p = pos[m];
   uint16_t* o = out + (m * heads + h) * D;
   if (p < 0 || p >= max_pos) {
-    o[i] = 0;
-    o[i + HALF] = 0;
+    *(u32x2_t*)(o + i) = u32x2_t{0u, 0u};
+    *(u32x2_t*)(o + i + HALF) = u32x2_t{0u, 0u};
     return;
   }
   const uint16_t* xr = x + m * x_stride + (int64_t)h * D;
-  const float c = cos_t[p * HALF + i];
-  const float s = sin_t[p * HALF + i];
-  const float a = __uint_as_float((uint32_t)xr[i] << 16);
-  const float b = __uint_as_float((uint32_t)xr[i + HALF] << 16);
-  const float ac = a * c, bs = b * s;  // rounded products (no contraction)
-  const float bc = b * c, as = a * s;
-  o[i] = (uint16_t)f32_to_bf16_bits(ac - bs);
-  o[i + HALF] = (uint16_t)f32_to_bf16_bits(bc + as);
+  const u32x2_t lo = *(const u32x2_t*)(xr + i);         // x_i .. x_{i+3}
+  const u32x2_t hi = *(const u32x2_t*)(xr + i + HALF);  // x_{i+64} .. x_{i+67}
+  const f32x4_t c = *(const f32x4_t*)(cos_t + p * HALF + i);
+  const f32x4_t s = *(const f32x4_t*)(sin_t + p * HALF + i);
+  const float a[4] = {bf16_lo(lo.x), bf16_hi(lo.x), bf16_lo(lo.y), bf16_hi(lo.y)};
+  const float b[4] = {bf16_lo(hi.x), bf16_hi(hi.x), bf16_lo(hi.y), bf16_hi(hi.y)};
+  float r0[4], r1[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float ac = a[j] * c[j], bs = b[j] * s[j];  // rounded products (no contraction)
+    const float bc = b[j] * c[j], as = a[j] * s[j];
+    r0[j] = ac - bs;
+    r1[j] = bc + as;
+  }
+  *(u32x2_t*)(o + i) = u32x2_t{pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3])};
+  *(u32x2_t*)(o + i + HALF) = u32x2_t{pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
 }
 
 // ---------------------------------------------------------------------------
@@ -166,8 +177,8 @@ int rope_table_host(double theta, int D, int64_t max_pos, float* cos_t, float* s
 int launch_rope(const uint16_t* x, int64_t x_stride, uint16_t* out, const int32_t* pos,
                 const float* cos_t, const float* sin_t, int64_t M, int heads, int64_t max_pos,
                 hipStream_t stream) {
-  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)M, (unsigned)heads), dim3(64), 0, stream, x,
-                     x_stride, out, pos, cos_t, sin_t, heads, max_pos);
+  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)M, (unsigned)((heads + 15) / 16)), dim3(256), 0,
+                     stream, x, x_stride, out, pos, cos_t, sin_t, heads, max_pos);
   return last_status();
 }
 

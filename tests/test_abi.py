@@ -156,6 +156,8 @@ def test_layer_step_argument_checks(lib):
     assert lib.bi_rope(P(ok), 512, P(ok), P(ok), P(ok), P(ok), 1, 4, 64, 8, None) == -3  # D
     assert lib.bi_rope(P(ok), 256, P(ok), P(ok), P(ok), P(ok), 1, 4, 128, 8, None) == -2  # stride
     assert lib.bi_rope(P(ok), 512, None, P(ok), P(ok), P(ok), 1, 4, 128, 8, None) == -1
+    assert lib.bi_rope(P(ok), 514, P(ok), P(ok), P(ok), P(ok), 1, 4, 128, 8, None) == -3  # stride % 4
+    assert lib.bi_rope(P(ok + 4), 512, P(ok), P(ok), P(ok), P(ok), 1, 4, 128, 8, None) == -3
     assert lib.bi_kv_append(P(ok), 1024, P(ok), 1024, P(ok), P(ok), P(ok), 1, 8, 128, 32, 4, 4,
                             None) == -3                                  # page size
     assert lib.bi_kv_append(P(ok), 1028, P(ok), 1024, P(ok), P(ok), P(ok), 1, 8, 128, 16, 4, 4,
