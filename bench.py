@@ -268,7 +268,7 @@ def main():
         # captured graph of back-to-back calls (weights rotated), so neither
         # Python nor launch overhead sits between kernels
         per = {}
-        for Mx in sorted(set([M, args.decode_m, 1])):
+        for Mx in sorted(set([M, args.decode_m, 1, 64, 256])):
             ax = make_acts(torch, synth, Mx, dev, seed=1) if Mx != M else acts
             ox = {name: torch.empty((Mx, N), dtype=torch.bfloat16, device=dev)
                   for name, K, N in LINEARS}
