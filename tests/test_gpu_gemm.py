@@ -122,7 +122,7 @@ def test_segment_starts_from_zero(gpu, M, row):
 
 def test_inblock_probe_is_recorded(gpu):
     """Three products in one 32-deep block: the oracle's left-to-right model
-    gives 0.0; the matrix core's own grouping is recorded, not judged."""
+    gives 0.0; the matrix core's own grouping is recorded, not asserted."""
     x, w = ordering_case(32, {0: (1.0, 1.0), 1: (BIG, BIG), 2: (-BIG, BIG)}, 1, 0)
     y = gpu.gemm(synth.from_bits(x, DEV), synth.from_bits(w, DEV))
     torch.cuda.synchronize()
