@@ -181,3 +181,30 @@ def test_fast_twin_parity(gpu, M):
     torch.cuda.synchronize()
     rows = sorted(set([0, M // 2, M - 1]))
     check_close_bf16(bits(y[rows]), oracle.gemm(bits(x[rows]), bits(w)), what=f"fast M={M}")
+
+
+def test_special_values_are_row_invariant(gpu):
+    """x rows holding +-inf, NaN, -0 and subnormal bf16 values: every row at
+    M = 1 (skinny path), inside M = 200 (slice path) and inside M = 2048
+    (tile path) gives the same bits, including NaN and infinity results."""
+    K, N = 4096, 4096
+    x = synth.bf16_normal((2048, K), seed=21, device=DEV)
+    w = synth.bf16_normal((K, N), seed=22, std=0.02, device=DEV)
+    xb = x.view(torch.int16)
+    special = torch.tensor([0x7F80, -128, 0x7FC0, -32768, 0x0001, -32767], dtype=torch.int16,
+                           device=DEV)                       # +inf -inf nan -0 sub -sub
+    for i, v in enumerate(special):
+        xb[3 * i + 1, 100 * i + 7] = v
+        xb[3 * i + 2, :] = v if i in (3, 4, 5) else xb[3 * i + 2, :]
+    full = gpu.gemm(x, w)
+    mid = gpu.gemm(x[:200].contiguous(), w)
+    torch.cuda.synchronize()
+    assert same_bits(mid, full[:200])
+    for r in range(20):
+        one = gpu.gemm(x[r:r + 1].contiguous(), w)
+        torch.cuda.synchronize()
+        assert same_bits(one, full[r:r + 1]), r
+    # the rows with an infinity or NaN produce non-finite outputs
+    f = full.float()
+    assert torch.isinf(f[1]).any() or torch.isnan(f[1]).any()
+    assert torch.isnan(f[7]).any()
