@@ -306,6 +306,7 @@ def main():
         extras["rmsnorm"] = bench_rmsnorm(torch, bi, synth, dev, args)
         extras["attention"] = bench_attn(torch, bi, synth, dev, args)
         extras["tp8_shard"] = bench_tp8(torch, bi, synth, dev, args)
+        extras["sample_us"] = bench_sample(torch, bi, synth, dev, args)
         extras["prefill_attention"] = bench_prefill_attn(torch, bi, synth, dev, args)
         extras["verify"] = bench_verify(torch, bi, synth, dev, args)
         result["extras"] = extras
@@ -506,6 +507,22 @@ def bench_tp8(torch, bi, synth, dev, args):
             row[f"fold_{name}_{S}seg"] = {"us": graph_time_us(
                 torch, lambda p, out: bi.gemm_fold(p, out), [(part, y)] * 8)}
         out[str(M)] = row
+    return out
+
+
+def bench_sample(torch, bi, synth, dev, args):
+    """bi_sample over a 128256-entry vocabulary at T = 0.8 for 1, 16 and 256
+    rows (graph replay of back-to-back calls)."""
+    import numpy as np
+    out = {}
+    for M in (1, 16, 256):
+        logits = synth.bf16_normal((M, 128256), seed=M, std=3.0, device=dev)
+        up = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)
+        seeds, steps = up(np.arange(M) + 7, np.uint64), up(np.arange(M) * 3, np.uint64)
+        temps = up(np.full(M, 0.8), np.float32)
+        tok = torch.empty(M, dtype=torch.int32, device=dev)
+        fn = lambda lg, sd, stp, tp, out: bi.sample(lg, sd, stp, tp, tokens=out)
+        out[str(M)] = graph_time_us(torch, fn, [(logits, seeds, steps, temps, tok)] * 8)
     return out
 
 

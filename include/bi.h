@@ -251,11 +251,17 @@ int bi_paged_prefill_attn(const bi_bf16 *q, const bi_bf16 *kv_pages,
  *   temperature[m] <= 0 or NaN: greedy, score = l;
  *   tokens[m] = the first index of the largest score (NaN counts as -inf).
  * logits [M, V] bf16; seeds, steps [M] uint64; temperature [M] fp32;
- * tokens [M] int32 out; all device memory.  V < 2^31.
+ * tokens [M] int32 out; all device memory.  1 <= M <= 65535, V < 2^31.
+ * ws: scratch of at least bi_sample_workspace_bytes(M) bytes (4-byte
+ * aligned, no initialisation): each row's vocabulary is split over 32
+ * workgroups whose best (score, index) pairs are then compared; the token
+ * does not depend on the split.
  * ---------------------------------------------------------------------- */
+size_t bi_sample_workspace_bytes(int64_t M);
 int bi_sample(const bi_bf16 *logits, int64_t M, int64_t V,
               const uint64_t *seeds, const uint64_t *steps,
-              const float *temperature, int32_t *tokens, void *stream);
+              const float *temperature, int32_t *tokens, void *ws,
+              size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Commit or rollback after a grouped verification pass (the LLM-42 digest,

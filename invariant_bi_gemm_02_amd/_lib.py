@@ -38,7 +38,8 @@ EXPORTS = ("bi_version", "bi_status_string", "bi_gemm_workspace_bytes", "bi_gemm
            "bi_attn_workspace_bytes", "bi_paged_decode_attn", "bi_attn_fast_workspace_bytes",
            "bi_paged_decode_attn_fast", "bi_embed", "bi_rope_table", "bi_rope", "bi_kv_append",
            "bi_silu_mul", "bi_add", "bi_paged_prefill_attn",
-           "bi_gemm_segments", "bi_gemm_fold", "bi_sample", "bi_verify_commit")
+           "bi_gemm_segments", "bi_gemm_fold", "bi_sample", "bi_verify_commit",
+           "bi_sample_workspace_bytes")
 
 _lock = threading.Lock()
 _lib = None
@@ -87,13 +88,15 @@ def load(path: str | None = None):
             "bi_paged_prefill_attn": [vp, vp, vp, vp, vp, vp, ctypes.POINTER(AttnDesc), i32, i32,
                                       vp, sz, vp],
             "bi_gemm_segments": [vp, vp, vp, i64, i64, i64, vp],
-            "bi_sample": [vp, i64, i64, vp, vp, vp, vp, vp],
+            "bi_sample": [vp, i64, i64, vp, vp, vp, vp, vp, sz, vp],
+            "bi_sample_workspace_bytes": [i64],
             "bi_verify_commit": [vp, vp, i32, vp, i32, vp, vp, vp, vp],
             "bi_gemm_fold": [vp, vp, i64, i64, i64, vp],
         }
         for f, a in sigs.items():
             getattr(lib, f).restype = ctypes.c_int
             getattr(lib, f).argtypes = a
+        lib.bi_sample_workspace_bytes.restype = sz
         _lib = lib
         return lib
 
@@ -446,7 +449,7 @@ def gemm_fold(part, y=None):
     return y
 
 
-def sample(logits, seeds, steps, temperature, tokens=None):
+def sample(logits, seeds, steps, temperature, tokens=None, ws: Workspace | None = None):
     """Per-row token of logits [M, V] (bf16): Gumbel-max with Philox noise
     keyed by (seeds[m], steps[m]) at temperature[m] > 0, else argmax."""
     lib = load()
@@ -458,8 +461,11 @@ def sample(logits, seeds, steps, temperature, tokens=None):
             raise ValueError(f"{n} must be a contiguous {dt} [M] tensor on the logits' device")
     if tokens is None:
         tokens = torch.empty(M, dtype=torch.int32, device=logits.device)
+    need = int(lib.bi_sample_workspace_bytes(M))
+    buf = _ws_for(logits.device, ws).get(need)
     st = lib.bi_sample(logits.data_ptr(), M, V, seeds.data_ptr(), steps.data_ptr(),
-                       temperature.data_ptr(), tokens.data_ptr(), _stream(logits.device))
+                       temperature.data_ptr(), tokens.data_ptr(), buf.data_ptr(), buf.numel(),
+                       _stream(logits.device))
     _raise(st, "bi_sample")
     return tokens
 

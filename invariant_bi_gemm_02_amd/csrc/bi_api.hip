@@ -151,15 +151,21 @@ int bi_gemm_fold(const float* part, bi_bf16* y, int64_t M, int64_t N, int64_t S,
   return bi::launch_gemm_fold(part, y, M, N, S, (hipStream_t)stream);
 }
 
+size_t bi_sample_workspace_bytes(int64_t M) { return M > 0 ? bi::sample_ws_bytes(M) : 0; }
+
 int bi_sample(const bi_bf16* logits, int64_t M, int64_t V, const uint64_t* seeds,
-              const uint64_t* steps, const float* temperature, int32_t* tokens, void* stream) {
+              const uint64_t* steps, const float* temperature, int32_t* tokens, void* ws,
+              size_t ws_bytes, void* stream) {
   if (!logits || !seeds || !steps || !temperature || !tokens) return BI_ERR_NULL;
-  if (M <= 0 || V <= 0 || M > 0x7fffffff || V >= kMaxElems || M * V >= kMaxElems * 64)
+  if (M <= 0 || V <= 0 || M > 65535 || V >= kMaxElems || M * V >= kMaxElems * 64)
     return BI_ERR_SHAPE;
   if (((uintptr_t)logits & 1u) || ((uintptr_t)seeds & 7u) || ((uintptr_t)steps & 7u) ||
       ((uintptr_t)temperature & 3u) || ((uintptr_t)tokens & 3u))
     return BI_ERR_UNSUPPORTED;
-  return bi::launch_sample(logits, M, V, seeds, steps, temperature, tokens, (hipStream_t)stream);
+  if (!ws || ws_bytes < bi::sample_ws_bytes(M)) return BI_ERR_WORKSPACE;
+  if ((uintptr_t)ws & 3u) return BI_ERR_UNSUPPORTED;
+  return bi::launch_sample(logits, M, V, seeds, steps, temperature, tokens, ws,
+                           (hipStream_t)stream);
 }
 
 int bi_verify_commit(const int32_t* candidates, const int32_t* verified, int32_t rows,

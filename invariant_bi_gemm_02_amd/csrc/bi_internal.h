@@ -26,8 +26,10 @@ int launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* block_tabl
                 const int32_t* ctx_lens, uint16_t* out, const bi_attn_desc* d, void* ws,
                 size_t ws_bytes, hipStream_t stream, bool fast, int num_cus);
 
+size_t sample_ws_bytes(int64_t M);
 int launch_sample(const uint16_t* logits, int64_t M, int64_t V, const uint64_t* seeds,
-                  const uint64_t* steps, const float* temps, int32_t* tokens, hipStream_t stream);
+                  const uint64_t* steps, const float* temps, int32_t* tokens, void* ws,
+                  hipStream_t stream);
 int launch_verify_commit(const int32_t* cand, const int32_t* ver, const int32_t* row_start, int R,
                          int rows, int32_t* accepted, int32_t* commit_len, int32_t* fix_token,
                          hipStream_t stream);

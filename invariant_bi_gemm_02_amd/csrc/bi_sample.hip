@@ -11,8 +11,9 @@
 //   T > 0      Gumbel-max: score = l / T + (-log(-log u)), fp32;
 //   T <= 0     greedy: score = l;
 //   token      the first index of the largest score (NaN counts as -inf).
-// The maximum with first-index ties is exact and order-free, so the
-// workgroup's reduction tree cannot change the token.
+// The maximum with first-index ties is exact and order-free, so neither the
+// split of the vocabulary over workgroups nor any reduction tree can change
+// the token.
 //
 // Commit or rollback (LLM-42 digest, method: a verified prefix is committed;
 // at the first mismatch the later candidates are discarded and decoding
@@ -50,23 +51,32 @@ __device__ __forceinline__ bool sample_better(float s, int i, float bs, int bi) 
   return s > bs || (s == bs && i < bi);
 }
 
-// grid = M, block = 1024: lane t takes vocabulary blocks t, t + 1024, ...
-// (4 entries each, one Philox call), then the workgroup reduces.
-__global__ __launch_bounds__(1024) void sample_kernel(const uint16_t* __restrict__ logits, int64_t V,
-                                                      const uint64_t* __restrict__ seeds,
-                                                      const uint64_t* __restrict__ steps,
-                                                      const float* __restrict__ temps,
-                                                      int32_t* __restrict__ tokens) {
-  __shared__ float rs[16];
-  __shared__ int ri[16];
-  const int64_t m = blockIdx.x;
+// Two launches.  sample_chunk_kernel: grid = (SMP_CHUNKS, M), block = 256;
+// workgroup p takes the vocabulary entries of chunk p (whole 4-entry Philox
+// blocks), lane t its blocks t, t + 256, ..., and writes the chunk's best
+// (score, index) to the workspace.  sample_pick_kernel: one 64-lane wave
+// per row takes the best of the chunks.  The maximum with first-index ties
+// is exact and does not depend on how the entries are grouped.
+static constexpr int SMP_CHUNKS = 32;
+
+__global__ __launch_bounds__(256) void sample_chunk_kernel(
+    const uint16_t* __restrict__ logits, int64_t V, const uint64_t* __restrict__ seeds,
+    const uint64_t* __restrict__ steps, const float* __restrict__ temps,
+    float* __restrict__ best_s, int32_t* __restrict__ best_i) {
+  __shared__ float rs[4];
+  __shared__ int ri[4];
+  const int p = blockIdx.x;
+  const int64_t m = blockIdx.y;
+  const int64_t nblk = (V + 3) / 4;
+  const int64_t per = (nblk + SMP_CHUNKS - 1) / SMP_CHUNKS;  // Philox blocks per chunk
+  const int64_t b0 = p * per, b1 = min(nblk, b0 + per);
   const uint16_t* row = logits + m * V;
   const float T = temps[m];
   const bool greedy = !(T > 0.0f);
   const uint64_t seed = seeds[m], step = steps[m];
   float best = -INFINITY;
   int bidx = 0x7fffffff;
-  for (int64_t b = threadIdx.x; b * 4 < V; b += 1024) {
+  for (int64_t b = b0 + threadIdx.x; b < b1; b += 256) {
     uint64_t r[4] = {0, 0, 0, 0};
     if (!greedy) philox4x64_10((uint64_t)b, step, 0, 0, seed, 0, r);
 #pragma unroll
@@ -108,13 +118,33 @@ __global__ __launch_bounds__(1024) void sample_kernel(const uint16_t* __restrict
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 16; ++w)
+    for (int w = 1; w < 4; ++w)
       if (sample_better(rs[w], ri[w], best, bidx)) {
         best = rs[w];
         bidx = ri[w];
       }
-    tokens[m] = bidx;
+    best_s[m * SMP_CHUNKS + p] = best;
+    best_i[m * SMP_CHUNKS + p] = bidx;
   }
+}
+
+__global__ __launch_bounds__(64) void sample_pick_kernel(const float* __restrict__ best_s,
+                                                         const int32_t* __restrict__ best_i,
+                                                         int32_t* __restrict__ tokens) {
+  const int64_t m = blockIdx.x;
+  const int l = threadIdx.x;
+  float best = l < SMP_CHUNKS ? best_s[m * SMP_CHUNKS + l] : -INFINITY;
+  int bidx = l < SMP_CHUNKS ? best_i[m * SMP_CHUNKS + l] : 0x7fffffff;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float os = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bidx, o, 64);
+    if (sample_better(os, oi, best, bidx)) {
+      best = os;
+      bidx = oi;
+    }
+  }
+  if (l == 0) tokens[m] = bidx;
 }
 
 // One lane per request: the window's leading matches are accepted; at the
@@ -135,10 +165,18 @@ __global__ __launch_bounds__(256) void verify_commit_kernel(
   fix_token[r] = a < w ? ver[s + a] : -1;
 }
 
+size_t sample_ws_bytes(int64_t M) { return (size_t)M * SMP_CHUNKS * 8; }
+
 int launch_sample(const uint16_t* logits, int64_t M, int64_t V, const uint64_t* seeds,
-                  const uint64_t* steps, const float* temps, int32_t* tokens, hipStream_t stream) {
-  hipLaunchKernelGGL(sample_kernel, dim3((unsigned)M), dim3(1024), 0, stream, logits, V, seeds,
-                     steps, temps, tokens);
+                  const uint64_t* steps, const float* temps, int32_t* tokens, void* ws,
+                  hipStream_t stream) {
+  float* bs = (float*)ws;
+  int32_t* bidx = (int32_t*)(bs + M * SMP_CHUNKS);
+  hipLaunchKernelGGL(sample_chunk_kernel, dim3(SMP_CHUNKS, (unsigned)M), dim3(256), 0, stream,
+                     logits, V, seeds, steps, temps, bs, bidx);
+  if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
+  hipLaunchKernelGGL(sample_pick_kernel, dim3((unsigned)M), dim3(64), 0, stream, bs, bidx,
+                     tokens);
   return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 

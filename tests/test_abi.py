@@ -84,9 +84,13 @@ def test_segment_and_fold_argument_checks(lib):
 
 def test_sample_and_commit_argument_checks(lib):
     ok = 0x1000
-    assert lib.bi_sample(None, 1, 10, P(ok), P(ok), P(ok), P(ok), None) == -1
-    assert lib.bi_sample(P(ok), 0, 10, P(ok), P(ok), P(ok), P(ok), None) == -2
-    assert lib.bi_sample(P(ok), 1, 10, P(ok + 4), P(ok), P(ok), P(ok), None) == -3  # seeds % 8
+    need = lib.bi_sample_workspace_bytes(3)
+    assert need == 3 * 32 * 8
+    assert lib.bi_sample(None, 1, 10, P(ok), P(ok), P(ok), P(ok), P(ok), need, None) == -1
+    assert lib.bi_sample(P(ok), 0, 10, P(ok), P(ok), P(ok), P(ok), P(ok), need, None) == -2
+    assert lib.bi_sample(P(ok), 1, 10, P(ok + 4), P(ok), P(ok), P(ok), P(ok), need,
+                         None) == -3                                    # seeds % 8
+    assert lib.bi_sample(P(ok), 3, 10, P(ok), P(ok), P(ok), P(ok), P(ok), need - 8, None) == -4
     assert lib.bi_verify_commit(P(ok), None, 4, P(ok), 1, P(ok), P(ok), P(ok), None) == -1
     assert lib.bi_verify_commit(P(ok), P(ok), 4, P(ok), 0, P(ok), P(ok), P(ok), None) == -2
     assert lib.bi_verify_commit(P(ok), P(ok), 4, P(ok + 2), 1, P(ok), P(ok), P(ok), None) == -3
