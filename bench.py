@@ -7,7 +7,8 @@ step's bi_gemm throughput in TFLOP/s.  The same run also reports, on the same
 kind of data:
   * the decode regime (M = 16): GB/s against the HBM roofline;
   * the invariance overhead t_bi / t_fast - 1 against the fast twins;
-  * bitwise mismatches between rows at M = 1 and the same rows in the batch;
+  * bitwise mismatches between rows at M = 1 and the same rows in the batch,
+    and the mismatch ratio of bi_gemm and of its fast twin on those rows;
   * bi_rmsnorm (x[512,4096]) and bi_paged_decode_attn (64 requests, context
     lengths uniform in [512, 32768]) with their HBM roofline fractions;
   * the CPU oracle timed on host cores on a bounded sample (rows of the same
@@ -295,14 +296,23 @@ def main():
                             "gbs": byt / (tot_b * 1e-6) / 1e9,
                             "hbm_frac": byt / (tot_b * 1e-6) / 1e9 / HBM_PEAK_GBS}
         extras["by_M"] = per
-        # bitwise invariance on this data: rows at M=1 vs rows in the batch
-        mism = 0
+        # bitwise invariance on this data: rows at M=1 vs rows in the batch,
+        # for bi_gemm and (as the contrast) for its fast twin
+        mism, mism_fast, compared = 0, 0, 0
         for name, K, N in LINEARS:
             y_full = bi.gemm(acts[name], wsets[0][name])
+            y_full_fast = bi.gemm_fast(acts[name], wsets[0][name])
             for r in (0, M // 2, M - 1):
-                y1 = bi.gemm(acts[name][r:r + 1].contiguous(), wsets[0][name])
+                x1 = acts[name][r:r + 1].contiguous()
+                y1 = bi.gemm(x1, wsets[0][name])
+                y1f = bi.gemm_fast(x1, wsets[0][name])
                 mism += int((y1.view(torch.int16) != y_full[r:r + 1].view(torch.int16)).sum())
+                mism_fast += int((y1f.view(torch.int16) !=
+                                  y_full_fast[r:r + 1].view(torch.int16)).sum())
+                compared += N
         extras["mismatches_m1_vs_batch"] = mism
+        extras["mismatch_ratio_m1_vs_batch"] = {"bi": mism / compared, "fast": mism_fast / compared,
+                                                "elements": compared}
         extras["rmsnorm"] = bench_rmsnorm(torch, bi, synth, dev, args)
         extras["attention"] = bench_attn(torch, bi, synth, dev, args)
         extras["tp8_shard"] = bench_tp8(torch, bi, synth, dev, args)

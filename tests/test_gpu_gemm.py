@@ -145,12 +145,14 @@ def test_m_sweep_bitwise_and_sampled_oracle(gpu, name, K, N):
     check_close_bf16(got, want, what=f"{name} sampled rows")
 
 
-@pytest.mark.parametrize("M,N,K", [(2048, 3136, 544), (1500, 4224, 1056), (700, 8256, 96)])
+@pytest.mark.parametrize("M,N,K", [(2048, 3136, 544), (1500, 4224, 1056), (700, 8256, 96),
+                                   (2048, 3136, 640), (2048, 3136, 576), (1500, 4224, 1216)])
 def test_tile_path_ragged_shapes(gpu, M, N, K):
     """Tile-path launches whose last tile column is half empty (N % 128 == 64),
     whose tile count is not a multiple of the 8 XCDs, and whose K ends in a
-    half stage: sampled rows match the skinny path bit for bit and the oracle
-    within tolerance."""
+    half stage (K % 64 == 32), in one whole stage (K % 512 == 64) or in a
+    partial segment of two or three stages (K % 512 == 128, 192): sampled rows
+    match the skinny path bit for bit and the oracle within tolerance."""
     x, w = synth.gemm_inputs(M, K, N, seed=M + K, device=DEV)
     y = gpu.gemm(x, w)
     rows = [0, 1, M // 2, M - 1]
