@@ -48,8 +48,11 @@ def gemm_bytes(M, K, N):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=40)
+    # the GPU's clocks keep rising for the first ~60 steps of back-to-back
+    # GEMMs (gate_up per launch: ~600 us at first, ~480 us from then on), so
+    # the untimed warm-up covers that ramp
+    p.add_argument("--warmup", type=int, default=60)
     p.add_argument("--m", type=int, default=2048)
     p.add_argument("--decode-m", type=int, default=16)
     p.add_argument("--no-cpu-baseline", action="store_true")
