@@ -122,7 +122,8 @@ int bi_gemm_fast(const bi_bf16 *x, const bi_bf16 *W, bi_bf16 *y,
  * bi_gemm_segments: part[s][m][n] (fp32, [ceil(K/512)][M][N], caller
  *   owned, 16-byte aligned) = sum over k in [512 s, min(512 s + 512, K)) of
  *   x[m][k] W[k][n], accumulated from +0 in bi_gemm's order.  x, W as for
- *   bi_gemm (same requirements); no workspace.
+ *   bi_gemm (same requirements, and N <= 2^21 when M > 64, else
+ *   BI_ERR_UNSUPPORTED); no workspace.
  * bi_gemm_fold: y[m][n] = bf16(((part[0] + part[1]) + ...) + part[S-1]),
  *   fp32 adds in index order, round to nearest even; part as above with S
  *   segments, M <= 65535, N % 64 == 0, 16-byte aligned pointers.

@@ -20,8 +20,9 @@
 //   gemm_fold_kernel    adds workspace segment sums in index order, narrows.
 //   gemm_tile_kernel    M > 64 (matrix-core bound): 256x128 output tiles, all
 //                       segments folded in registers; with too few tiles to
-//                       fill the chip, one workgroup per (tile, segment)
-//                       writes segment sums for gemm_fold_kernel instead.
+//                       fill the chip, one workgroup per (tile, run of
+//                       consecutive segments) writes each segment's sum for
+//                       gemm_fold_kernel instead.
 // Padding rows (>= M) load as zero through the buffer range check and are
 // never stored.
 //
@@ -228,9 +229,12 @@ __global__ __launch_bounds__(64) void gemm_fold_kernel(const float* __restrict__
 //
 // FOLD: segments of KC (a multiple of 64) from +0, folded in order into the
 // running total after each (batch-invariant schedule); the first K-block of
-// a segment is issued with a zero accumulator.  Without FOLD, one chain runs
-// over the workgroup's K range.  SLICE: the workgroup covers only K slice
-// blockIdx.y ([y*KC, y*KC + KC)) and writes its fp32 sum to part[y][M][N].
+// a segment is issued with a zero accumulator.  Without FOLD or SLICE, one
+// chain runs over all of K.  SLICE: the workgroup covers the spw consecutive
+// segments of KC from segment blockIdx.y * spw, each from +0, and writes
+// every segment's fp32 sum to part[segment][M][N] as it completes; the loads
+// run on through the segment boundaries.  (The fast twin slices with KC the
+// whole slice and spw = 1.)
 //
 // Workgroups are dispatched to the 8 XCDs round robin.  remap 2 gives each
 // XCD a band of whole tile columns, walked in groups of 4 tile rows, so that
@@ -249,7 +253,7 @@ __device__ __forceinline__ int tl_wphys(int r, int c) {
 template <bool FOLD, bool SLICE>
 __global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, uint16_t* __restrict__ y,
-    int M, int N, int K, int KC, int tm, int tn, int remap, float* __restrict__ part) {
+    int M, int N, int K, int KC, int tm, int tn, int remap, float* __restrict__ part, int spw) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * TL_STAGE];
 
   const int tid = threadIdx.x;
@@ -274,8 +278,9 @@ __global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
 
   const i32x4_t xr = make_rsrc_words(x, (uint32_t)((size_t)M * K * 2));
   const i32x4_t wr = make_rsrc_words(W, (uint32_t)((size_t)K * N * 2));
-  const int kbeg = SLICE ? (int)blockIdx.y * KC : 0;
-  const int kend = SLICE ? min(K, kbeg + KC) : K;
+  const int seg0 = SLICE ? (int)blockIdx.y * spw : 0;  // first segment (SLICE)
+  const int kbeg = SLICE ? seg0 * KC : 0;
+  const int kend = SLICE ? min(K, kbeg + spw * KC) : K;
   const int nstage = (kend - kbeg + TL_BK - 1) / TL_BK;
 
   // Each wave instruction fills 1 KB of a stage: wave w fills x regions
@@ -364,7 +369,14 @@ __global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
   };
   // One stage: K-block 0 (from +0 when it opens a segment), barrier, refill
   // of the buffer just consumed, next stage's K-block 0 fragments, K-block 1.
-  auto stage = [&](int st, auto zero) {
+  // SLICE: sixteen partial-sum stores per lane go out at each segment
+  // boundary, after the loads of the next two stages.  Stores count in vmcnt
+  // and complete in issue order, so the first two stages after a boundary
+  // wait for vmcnt(22) (their stage's six loads done; the next stage's six
+  // and the sixteen stores may be in flight) instead of vmcnt(6), and the
+  // ring keeps running.  The stores are issued unconditionally (out-of-range
+  // offsets are dropped by the buffer range check), so the count is exact.
+  auto stage = [&](int st, auto zero, bool after_store) {
     const bool two = kbeg + st * TL_BK + KB < kend;
     // read even when K-block 1 is past K (the fragments are then unused), so
     // that the LDS-counter waits see one path
@@ -377,7 +389,10 @@ __global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
     // this wave's loads of stage st+1 have landed (only stage st+2's six may
     // be in flight) and its reads of stage st are done; after the barrier
     // every wave's are, so stage st's buffer can be refilled
-    asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (SLICE && after_store)
+      asm volatile("s_waitcnt vmcnt(22) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     dma(st + 3);
     read_frags(st + 1, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -389,19 +404,54 @@ __global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
   dma(2);
   asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
   read_frags(0, 0);
-  const int sps = FOLD ? KC / TL_BK : nstage;  // stages per segment
-  int st = 0;
+  const int wrow0 = m0 + wm * 64;
+  // SLICE: the sixteen stores of segment sg's sums, one per (row group,
+  // column group) of the wave, each issued whatever the row and column
+  // (offsets of rows >= M or columns >= N lie past the buffer and are
+  // dropped).  The buffer starts at the tile's corner in part[sg], so the
+  // offsets stay below 256 N 4 bytes.
+  auto store_part = [&](int sg) {
+    const __amdgpu_buffer_rsrc_t pr =
+        make_rsrc(part + ((size_t)sg * M + m0) * N + n0,
+                  (uint32_t)min((size_t)0x7fffffff, ((size_t)min(TL_BM, M - m0) * N) * 4));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int r = wm * 64 + s * 16 + l16;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int c = wn * 64 + tt * 16 + g * 4;
+        // bit 31 set: past the buffer (at most 2^31 - 1 bytes).  Written as
+        // arithmetic, not a select, so that no branch can skip a store.
+        const uint32_t out = (uint32_t)(m0 + r >= M) | (uint32_t)(n0 + c >= N);
+        const uint32_t off = ((uint32_t)(r * N + c) * 4u) | (out << 31);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[s][tt]), pr, off, 0, 0);
+      }
+    }
+  };
+
+  const int sps = (FOLD || SLICE) ? KC / TL_BK : nstage;  // stages per segment
+  int st = 0, sg = seg0;
   for (;;) {
-    stage(st, std::true_type{});
     const int seg_end = min(nstage, st + sps);
-    for (++st; st < seg_end; ++st) stage(st, std::false_type{});
+    if constexpr (SLICE) {  // the first two stages of a segment wait past its boundary stores
+      stage(st++, std::true_type{}, sg > seg0);
+      if (st < seg_end) stage(st++, std::false_type{}, sg > seg0);
+    } else {
+      stage(st++, std::true_type{}, false);
+    }
+    for (; st < seg_end; ++st) stage(st, std::false_type{}, false);
     if (st >= nstage) break;
-    fold();
+    if (FOLD) fold();
+    if (SLICE) store_part(sg);
+    ++sg;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (FOLD) fold();
+  if (SLICE) {
+    store_part(sg);
+    return;
+  }
 
-  const int wrow0 = m0 + wm * 64;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int m = wrow0 + s * 16 + l16;
@@ -410,12 +460,8 @@ __global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
       for (int tt = 0; tt < 4; ++tt) {
         const f32x4_t v = FOLD ? tot[s][tt] : acc[s][tt];
         const int col = n0 + wn * 64 + tt * 16 + g * 4;
-        if (SLICE) {
-          *(f32x4_t*)&part[((size_t)blockIdx.y * M + m) * N + col] = v;
-        } else {
-          *(u32x2_t*)&y[(size_t)m * N + col] =
-              u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        }
+        *(u32x2_t*)&y[(size_t)m * N + col] =
+            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
     }
   }
@@ -450,6 +496,28 @@ int64_t fast_split_kc(int64_t M, int64_t N, int64_t K, int num_cus) {
   const int64_t slices = std::max<int64_t>(1, ceil_div(std::max(num_cus, 1), tiles));
   return ceil_div(ceil_div(K, slices), TL_BK) * TL_BK;
 }
+// The K-slice kernel addresses a tile's partial sums with 32-bit offsets
+// below 2^31 (256 rows of N floats).
+static constexpr int64_t SLICE_MAX_N = 1 << 21;
+
+// Segments per workgroup on the invariant K-slice path: the count g whose
+// critical path, g segments times the rounds that tiles * ceil(S / g)
+// workgroups take on a 256-CU chip, is shortest (the largest such g: fewer
+// workgroups, fewer pipeline fills).  Each segment is still summed from +0
+// and stored on its own, so g moves work between workgroups and never
+// changes the bits.
+static int64_t segments_per_slice(int64_t tiles, int64_t S) {
+  int64_t best = 1, best_cost = INT64_MAX;
+  for (int64_t g = 1; g <= S; ++g) {
+    const int64_t cost = g * ceil_div(tiles * ceil_div(S, g), 256);
+    if (cost <= best_cost) {
+      best = g;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 static int64_t slice_kc(int64_t M, int64_t N, int64_t K, bool fast, int num_cus) {
   return fast ? fast_split_kc(M, N, K, num_cus) : BI_KC;
 }
@@ -472,20 +540,24 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
       dim3 grid((unsigned)(tm * tn));
       if (fast)
         hipLaunchKernelGGL((gemm_tile_kernel<false, false>), grid, dim3(512), 0, stream, x, W, y,
-                           (int)M, (int)N, (int)K, (int)K, (int)tm, (int)tn, remap, (float*)nullptr);
+                           (int)M, (int)N, (int)K, (int)K, (int)tm, (int)tn, remap, (float*)nullptr,
+                           1);
       else
         hipLaunchKernelGGL((gemm_tile_kernel<true, false>), grid, dim3(512), 0, stream, x, W, y,
-                           (int)M, (int)N, (int)K, BI_KC, (int)tm, (int)tn, remap, (float*)nullptr);
+                           (int)M, (int)N, (int)K, BI_KC, (int)tm, (int)tn, remap, (float*)nullptr,
+                           1);
       return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
     }
     const int64_t kc = slice_kc(M, N, K, fast, num_cus);
     const int64_t ns = ceil_div(K, kc);
-    if (ns > 65535) return BI_ERR_UNSUPPORTED;
+    if (ns > 65535 || N > SLICE_MAX_N) return BI_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < (size_t)ns * (size_t)M * (size_t)N * sizeof(float)) return BI_ERR_WORKSPACE;
     float* part = (float*)ws;
-    hipLaunchKernelGGL((gemm_tile_kernel<false, true>), dim3((unsigned)(tm * tn), (unsigned)ns),
-                       dim3(512), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)kc, (int)tm,
-                       (int)tn, remap, part);
+    const int64_t spw = fast ? 1 : segments_per_slice(tm * tn, ns);
+    hipLaunchKernelGGL((gemm_tile_kernel<false, true>),
+                       dim3((unsigned)(tm * tn), (unsigned)ceil_div(ns, spw)), dim3(512), 0, stream,
+                       x, W, y, (int)M, (int)N, (int)K, (int)kc, (int)tm, (int)tn, remap, part,
+                       (int)spw);
     if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
     hipLaunchKernelGGL(gemm_fold_kernel, dim3((unsigned)ceil_div(N, 256), (unsigned)M), dim3(64),
                        0, stream, part, y, (int)M, (int)N, (int)ns);
@@ -531,11 +603,14 @@ int launch_gemm_segments(const uint16_t* x, const uint16_t* W, float* part, int6
                          (int)N, (int)K);
     return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
   }
+  if (N > SLICE_MAX_N) return BI_ERR_UNSUPPORTED;
   const int64_t tm = ceil_div(M, TILE_BM), tn = ceil_div(N, TL_BN);
   const int remap = (tn % 8 == 0) ? 2 : ((tm * tn) % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((gemm_tile_kernel<false, true>), dim3((unsigned)(tm * tn), (unsigned)S),
-                     dim3(512), 0, stream, x, W, (uint16_t*)nullptr, (int)M, (int)N, (int)K, BI_KC,
-                     (int)tm, (int)tn, remap, part);
+  const int64_t spw = segments_per_slice(tm * tn, S);
+  hipLaunchKernelGGL((gemm_tile_kernel<false, true>),
+                     dim3((unsigned)(tm * tn), (unsigned)ceil_div(S, spw)), dim3(512), 0, stream,
+                     x, W, (uint16_t*)nullptr, (int)M, (int)N, (int)K, BI_KC, (int)tm, (int)tn,
+                     remap, part, (int)spw);
   return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 
