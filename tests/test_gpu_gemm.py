@@ -162,6 +162,29 @@ def test_tile_path_ragged_shapes(gpu, M, N, K):
     check_close_bf16(bits(y[rows]), oracle.gemm(bits(x[rows]), bits(w)), what=f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(200, 4160, 14432), (256, 4096, 14656), (300, 4032, 14336)])
+def test_slice_path_runs_of_segments(gpu, M, N, K):
+    """Mid-size M with few tiles: one workgroup runs several consecutive
+    512-row segments and stores each segment's sum.  The shapes give 2, 4 and
+    7 segments per workgroup with a last run of one segment (29 segments), a
+    last segment of 1.5 and 5 stages, a half-empty last tile column and a
+    second tile row of 44 rows.  The workspace is filled with NaN first, so a
+    sum that is not stored cannot pass on stale values.  Every row of the
+    first 64 matches the skinny path bit for bit (one call at M = 64), sampled
+    rows match single-row calls, and the oracle within tolerance."""
+    x, w = synth.gemm_inputs(M, K, N, seed=M + N + K, device=DEV)
+    ws = gpu.Workspace(DEV)
+    ws.get(gpu.gemm_workspace_bytes(M, N, K)).view(torch.float32).fill_(float("nan"))
+    y = gpu.gemm(x, w, ws=ws)
+    assert same_bits(gpu.gemm(x[:64].contiguous(), w), y[:64])
+    rows = [0, 100, M - 1]
+    for r in rows:
+        assert same_bits(gpu.gemm(x[r:r + 1].contiguous(), w), y[r:r + 1]), f"row {r}"
+    torch.cuda.synchronize()
+    assert not torch.isnan(y.float()).any()
+    check_close_bf16(bits(y[rows]), oracle.gemm(bits(x[rows]), bits(w)), what=f"{M}x{N}x{K}")
+
+
 def test_run_to_run_and_row_permutation(gpu):
     x, w = synth.gemm_inputs(300, 4096, 4096, seed=4, device=DEV)
     base = gpu.gemm(x, w)
