@@ -86,6 +86,12 @@ class Timer:
     def mean_ms(self):
         return self.total_ms() / max(1, len(self.pairs))
 
+    def percentiles_us(self):
+        import numpy as np
+        t = np.array([a.elapsed_time(b) for a, b in self.pairs]) * 1e3
+        return {"p10": float(np.percentile(t, 10)), "p50": float(np.percentile(t, 50)),
+                "p90": float(np.percentile(t, 90))}
+
 
 def graph_time_us(torch, fn, calls, replays=3):
     """Mean time per call of `fn(*args, out=o)` over back-to-back calls
@@ -250,6 +256,7 @@ def main():
                 "avg_launch_us": gu_ms * 1e3}
 
     roof["traffic"] = measured_traffic(M)
+    roof["launch_us_percentiles"] = per_kernel["gate_up"].percentiles_us()
     result = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
@@ -322,12 +329,54 @@ def main():
         extras["sample_us"] = bench_sample(torch, bi, synth, dev, args)
         extras["prefill_attention"] = bench_prefill_attn(torch, bi, synth, dev, args)
         extras["verify"] = bench_verify(torch, bi, synth, dev, args)
+        extras["ceilings"] = bench_ceilings(torch, synth, dev, M)
         result["extras"] = extras
 
     if not args.no_cpu_baseline:
         import oracle
         result["cpu_baseline"] = cpu_baseline(synth, oracle, M)
     print(json.dumps(result))
+
+
+def bench_ceilings(torch, synth, dev, M):
+    """Measured ceilings on this machine, for context beside the spec peaks: a
+    plain 1 GiB device copy (bytes read + written per second), and torch's
+    bf16 matmul (the vendor library, not batch-invariant) on the dominant
+    linear, gate_up 4096->28672 at the bench's M, with the same rotated
+    weights and inputs resident in HBM."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    for _ in range(10):
+        e = t.start()
+        b.copy_(a)
+        t.stop(e)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n / (t.mean_ms() * 1e-3) / 1e9
+    del a, b
+    K, N = 4096, 28672
+    x = synth.bf16_normal((M, K), seed=9, device=dev)
+    ws = [synth.bf16_normal((K, N), seed=90 + i, std=0.02, device=dev) for i in range(2)]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    for i in range(40):
+        torch.matmul(x, ws[i % 2], out=y)
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    for i in range(20):
+        e = t.start()
+        torch.matmul(x, ws[i % 2], out=y)
+        t.stop(e)
+    torch.cuda.synchronize()
+    us = t.mean_ms() * 1e3
+    return {"copy_1gib_gbs": copy_gbs, "copy_frac_of_8tbs": copy_gbs / HBM_PEAK_GBS,
+            "torch_matmul_gate_up": {"M": M, "us": us,
+                                     "tflops": gemm_flops(M, K, N) / (us * 1e-6) / 1e12,
+                                     "note": "vendor library (hipBLASLt), not batch-invariant"}}
 
 
 def bench_rmsnorm(torch, bi, synth, dev, args):
