@@ -240,6 +240,11 @@ __global__ __launch_bounds__(64) void gemm_fold_kernel(const float* __restrict__
 // XCD a band of whole tile columns, walked in groups of 4 tile rows, so that
 // the 32 workgroups an XCD runs at once share 4 x panels and 8 W panels in
 // its L2; remap 1 gives each XCD a contiguous band of tiles, m fastest.
+// remap 3 (tile rows a multiple of 8) keeps those 4 x 8 groups but gives
+// XCDs x and x + 4 the same band of tile columns, upper and lower half of
+// the tile rows, walked in step: each W line is then wanted by two XCDs at
+// about the same time, so one of them finds it in the memory-side cache
+// rather than HBM (remap 2 reads a band's W twice, half a launch apart).
 static constexpr int TL_BM = 256, TL_BN = 128, TL_BK = 64;
 static constexpr int TL_XS = TL_BM * TL_BK;             // x slab elements (32 KB)
 static constexpr int TL_STAGE = TL_XS + TL_BK * TL_BN;  // + W slab (16 KB)
@@ -267,6 +272,11 @@ __global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
   int t = blockIdx.x;
   if (remap == 1) {
     t = (t & 7) * ((tm * tn) >> 3) + (t >> 3);
+  } else if (remap == 3) {
+    const int ncols = tn >> 2, xcd = t & 7, i = t >> 3, pr = xcd & 3, h = xcd >> 2, th = tm >> 1;
+    const int first = (i / (4 * ncols)) * 4, gm = min(4, th - first);
+    const int r = i - first * ncols;
+    t = (pr * ncols + r / gm) * tm + h * th + first + r % gm;
   } else if (remap == 2) {
     const int ncols = tn >> 3, xcd = t & 7, i = t >> 3;
     const int first = (i / (4 * ncols)) * 4, gm = min(4, tm - first);
@@ -535,7 +545,10 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
   const GemmPath p = gemm_path(M, N);
   if (p == GemmPath::Tile || p == GemmPath::TileSlice) {
     const int64_t tm = ceil_div(M, TILE_BM), tn = ceil_div(N, TL_BN);
-    const int remap = (tn % 8 == 0) ? 2 : ((tm * tn) % 8 == 0) ? 1 : 0;
+    const int remap = (tm % 8 == 0 && tn % 4 == 0) ? 3
+                      : (tn % 8 == 0)                 ? 2
+                      : ((tm * tn) % 8 == 0)          ? 1
+                                                      : 0;
     if (p == GemmPath::Tile) {
       dim3 grid((unsigned)(tm * tn));
       if (fast)
