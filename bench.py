@@ -398,9 +398,11 @@ def bench_verify(torch, bi, synth, dev, args):
     """LLM-42-style grouped verification on the Llama-3-8B-shaped decoder
     (32 layers, random init): 6 requests with prompts of 64..2048 tokens are
     prefilled in one multi-query pass (timed), then 256 window tokens split
-    over them are verified grouped (timed); counts logits that differ
-    between grouped and alone runs, and between the prefill pass and each
-    prompt's last token recomputed alone."""
+    over them are verified grouped (timed): rows grouped by request through
+    the multi-query attention, and the same rows shuffled through the per-row
+    decode attention.  Counts logits that differ between those two, between
+    grouped and alone runs, and between the prefill pass and each prompt's
+    last token recomputed alone."""
     import numpy as np
     from invariant_bi_gemm_02_amd.decoder import Decoder
     cfg = synth.LLAMA3_8B
@@ -434,25 +436,37 @@ def bench_verify(torch, bi, synth, dev, args):
            for r, n in enumerate(sizes) for i in range(n)]
     win = [win[i] for i in rng.permutation(len(win))]
     rid, pos, tok = map(np.array, zip(*win))
+    order = np.lexsort((pos, rid))          # windows grouped by request, in position order
+    inv = np.empty_like(order)
+    inv[order] = np.arange(len(order))
+    # the window as an engine batches it: rows grouped by request, so the
+    # multi-query attention reads each request's K/V once per block of rows
+    segs_w = [(r, pos[order][rid[order] == r], tok[order][rid[order] == r])
+              for r in range(len(sizes))]
+    g_rows = dec.prepare(*synth.grouped_rows(req, segs_w))
+    # the same rows in the shuffled order, attention per row (decode entry point)
     rows = dec.prepare(*req.rows(rid, pos, tok))
-    grouped = dec.run(rows)
+    shuffled = dec.run(rows)
+    g_logits = dec.run(g_rows)              # rows in `order`
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 5
-    e0.record()
-    for _ in range(reps):
-        dec.run(rows)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    timing = {}
+    for name, rr in (("grouped", g_rows), ("rows", rows)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dec.run(rr)
+        e1.record()
+        torch.cuda.synchronize()
+        timing[name] = e0.elapsed_time(e1) / reps
+    ms = timing["grouped"]
+    grouped = g_logits[torch.from_numpy(inv).to(dev)]     # back to the shuffled order
+    cross_mism = int((grouped.view(torch.int16) != shuffled.view(torch.int16)).sum())
+    del shuffled
     # per-request sampling of the window (seed per request, step = the
     # position sampled) and the commit-or-rollback step, with candidates that
     # diverge from the recompute at a drawn point of each window
     up = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)
-    order = np.lexsort((pos, rid))          # windows grouped by request, in position order
-    inv = np.empty_like(order)
-    inv[order] = np.arange(len(order))
-    g_logits = grouped[torch.from_numpy(order).to(dev)].contiguous()
     seeds = up(1000003 * rid[order] + 17, np.uint64)
     steps = up(pos[order] + 1, np.uint64)
     temps = up(np.full(len(win), 0.8), np.float32)
@@ -491,6 +505,8 @@ def bench_verify(torch, bi, synth, dev, args):
            "logit_mismatches_prefill_vs_last_token_alone": pre_mism,
            "ms_per_verify": ms,
            "tokens_per_s": len(win) / (ms * 1e-3), "logit_mismatches_grouped_vs_alone": mism,
+           "ms_per_verify_shuffled_rows_decode_attention": timing["rows"],
+           "logit_mismatches_multiquery_vs_shuffled_decode_rows": cross_mism,
            "ms_sample_and_commit": ms_commit,
            "sampled_token_mismatches_grouped_vs_alone": tok_mism,
            "accepted_per_request": [int(v) for v in acc.cpu()],

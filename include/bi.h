@@ -214,7 +214,9 @@ int bi_paged_decode_attn_fast(const bi_bf16 *q, const bi_bf16 *kv_pages,
  * output is bitwise what bi_paged_decode_attn gives it (prefill/decode
  * invariance, the property the LLM-42 digest notes its own method lacks).
  * Rows of a request share its KV cache; a workgroup loads every K/V tile
- * once for up to 64/G rows.
+ * once for up to 64/G rows.  With few rows the chunks of a row block are
+ * also split over workgroups and folded in chunk order by the combine of
+ * the decode entry point (same bits).
  *
  * q:           [rows, num_q_heads, head_dim] bf16, rows grouped by request.
  * kv_pages:    as for bi_paged_decode_attn.

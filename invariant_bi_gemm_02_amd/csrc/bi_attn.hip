@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ row_start,
     const int32_t* __restrict__ ctx_lens, float* __restrict__ part, uint16_t* __restrict__ out,
     int Hq, int Hkv, int requests, int max_blocks, long long num_pages, int max_ctx,
-    int nc_stride, int row_blocks, int rows, float scale) {
+    int nc_stride, int row_blocks, int rows, int cpw, float scale) {
   constexpr int QB = 64 / G;   // rows per workgroup
   constexpr int RPW = 16 / G;  // rows per wave
   constexpr int PU = 1;        // tokens per step of the P V loop
@@ -349,14 +349,19 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_kernel(
   const uint32_t* vcol = (const uint32_t*)vs + lane;
   const float* pwv = &pw[wave][0][0];
 
-  load_tile(0, min(ATILE, lmax));
-  for (int t0 = 0; t0 < lmax; t0 += ATILE) {
-    const int nt = min(ATILE, lmax - t0);  // tiles never straddle a chunk
+  // this workgroup's chunks: [cpw * blockIdx.y, cpw * blockIdx.y + cpw)
+  const int t_lo = (int)blockIdx.y * cpw * ACHUNK;
+  const int t_hi = (int)min((long long)lmax, (long long)t_lo + (long long)cpw * ACHUNK);
+  if (t_lo >= lmax) return;
+  load_tile(t_lo, min(ATILE, t_hi - t_lo));
+  for (int t0 = t_lo; t0 < t_hi; t0 += ATILE) {
+    // t_hi is lmax or a chunk boundary: tiles never straddle a chunk
+    const int nt = min(ATILE, t_hi - t0);
     __syncthreads();  // previous tile fully consumed
     store_tile();
     __syncthreads();
     const int t1 = t0 + ATILE;
-    if (t1 < lmax) load_tile(t1, min(ATILE, lmax - t1));
+    if (t1 < t_hi) load_tile(t1, min(ATILE, t_hi - t1));
     if (!wave_live) continue;
     if (t0 % ACHUNK == 0) {  // a chunk starts: fresh online-softmax state
       m_c = -INFINITY;
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_kernel(
     // [row][h][chunk][m, l, -, -, acc].  Column j of the wave is row
     // 16w/G + j/G, head j%G; the strides pass through an empty asm so that
     // the sixteen addresses are formed here rather than held across the loop.
-    if (t1 % ACHUNK == 0 || t1 >= lmax) {
+    if (t1 % ACHUNK == 0 || t1 >= t_hi) {
       const int c = t0 / ACHUNK;
       int hs = nc_stride * APART;
       asm volatile("" : "+s"(hs));
@@ -509,7 +514,9 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_kernel(
   // The combine, as the combine kernel does it, for the wave's columns: the
   // workgroup has written every chunk partial of its rows.  M* = max m_c,
   // w_c = exp(m_c - M*), L and O folded in chunk order, out = bf16(O / L).
-  if (!wave_live) return;
+  // With the chunks split over workgroups (gridDim.y > 1) the combine kernel
+  // runs afterwards instead.
+  if (!wave_live || gridDim.y > 1) return;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   int hs = nc_stride * APART;
@@ -684,12 +691,22 @@ int launch_prefill_attn(const uint16_t* q, const uint16_t* kv, const int32_t* bl
   const long long row_blocks = (max_rows_per_request + qb - 1) / qb;
   const long long nwg = (long long)d->num_kv_heads * requests * row_blocks;
   if (nwg > 0x7fffffffLL) return BI_ERR_UNSUPPORTED;
+  // Few row blocks (a verify window of a few rows per request over long
+  // contexts): split each block's chunks over several workgroups, up to about
+  // 2048 workgroups in all, and combine in a second kernel.  Many row blocks
+  // (a prefill): one workgroup walks all of a block's chunks and combines
+  // them itself.  Either way every chunk is computed as in the decode entry
+  // point and combined in chunk order, so the split never changes the bits.
+  const long long groups = std::max(1LL, std::min((long long)ncs, (2048 + nwg - 1) / nwg));
+  const int cpw = (int)((ncs + groups - 1) / groups);
+  const long long ngy = (ncs + cpw - 1) / cpw;
+  if (ngy > 65535) return BI_ERR_UNSUPPORTED;
   float* part = (float*)ws;
 #define BI_PREFILL_LAUNCH(GG)                                                                  \
-  hipLaunchKernelGGL(attn_prefill_kernel<GG>, dim3((unsigned)nwg), dim3(256), 0, stream, q,   \
-                     kv, block_table, row_start, ctx_lens, part, out, d->num_q_heads,         \
+  hipLaunchKernelGGL(attn_prefill_kernel<GG>, dim3((unsigned)nwg, (unsigned)ngy), dim3(256), 0, \
+                     stream, q, kv, block_table, row_start, ctx_lens, part, out, d->num_q_heads, \
                      d->num_kv_heads, requests, d->max_blocks_per_seq, (long long)d->num_pages, \
-                     d->max_ctx_len, ncs, (int)row_blocks, d->batch, d->scale)
+                     d->max_ctx_len, ncs, (int)row_blocks, d->batch, cpw, d->scale)
   switch (G) {
     case 1: BI_PREFILL_LAUNCH(1); break;
     case 2: BI_PREFILL_LAUNCH(2); break;
@@ -698,6 +715,12 @@ int launch_prefill_attn(const uint16_t* q, const uint16_t* kv, const int32_t* bl
     default: return BI_ERR_UNSUPPORTED;
   }
 #undef BI_PREFILL_LAUNCH
+  if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
+  if (ngy > 1) {
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)d->num_q_heads, (unsigned)d->batch),
+                       dim3(128), 0, stream, part, ctx_lens, out, d->num_q_heads, d->max_ctx_len,
+                       ncs, ACHUNK, 0);
+  }
   return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 
