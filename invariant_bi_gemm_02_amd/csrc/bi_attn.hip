@@ -691,13 +691,15 @@ int launch_prefill_attn(const uint16_t* q, const uint16_t* kv, const int32_t* bl
   const long long row_blocks = (max_rows_per_request + qb - 1) / qb;
   const long long nwg = (long long)d->num_kv_heads * requests * row_blocks;
   if (nwg > 0x7fffffffLL) return BI_ERR_UNSUPPORTED;
-  // Few row blocks (a verify window of a few rows per request over long
-  // contexts): split each block's chunks over several workgroups, up to about
-  // 2048 workgroups in all, and combine in a second kernel.  Many row blocks
-  // (a prefill): one workgroup walks all of a block's chunks and combines
-  // them itself.  Either way every chunk is computed as in the decode entry
-  // point and combined in chunk order, so the split never changes the bits.
-  const long long groups = std::max(1LL, std::min((long long)ncs, (2048 + nwg - 1) / nwg));
+  // Few row blocks (under 2048 workgroups: a verify window of a few rows per
+  // request over long contexts): split each block's chunks over several
+  // workgroups, toward 8192 in all, and combine in a second kernel.  Many
+  // row blocks (a prefill): one workgroup walks all of a block's chunks and
+  // combines them itself.  Either way every chunk is computed as in the
+  // decode entry point and combined in chunk order, so the split never
+  // changes the bits.
+  const long long groups =
+      nwg >= 2048 ? 1 : std::max(1LL, std::min((long long)ncs, (8192 + nwg - 1) / nwg));
   const int cpw = (int)((ncs + groups - 1) / groups);
   const long long ngy = (ncs + cpw - 1) / cpw;
   if (ngy > 65535) return BI_ERR_UNSUPPORTED;
