@@ -115,6 +115,35 @@ def graph_time_us(torch, fn, calls, replays=3):
     return e0.elapsed_time(e1) * 1e3 / (replays * len(calls))
 
 
+def paired_graph_time_us(torch, fa, fb, calls, rounds=5):
+    """Median time per call of fa and of fb over `calls`, each captured in
+    its own graph and replayed alternately, so that clock drift during the
+    measurement falls on both alike."""
+    graphs = []
+    for fn in (fa, fb):
+        for *a, oo in calls[:2]:
+            fn(*a, out=oo)      # workspace allocation happens outside capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for *a, oo in calls:
+                fn(*a, out=oo)
+        g.replay()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    ts = ([], [])
+    for _ in range(rounds):
+        for i, g in enumerate(graphs):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts[i].append(e0.elapsed_time(e1) * 1e3 / len(calls))
+    return sorted(ts[0])[rounds // 2], sorted(ts[1])[rounds // 2]
+
+
 def measured_traffic(M):
     """HBM bytes per launch of the dominant kernel (gate_up) from the committed
     rocprofv3 FETCH_SIZE/WRITE_SIZE runs, calibrated against a plain copy; None
@@ -283,13 +312,12 @@ def main():
             ax = make_acts(torch, synth, Mx, dev, seed=1) if Mx != M else acts
             ox = {name: torch.empty((Mx, N), dtype=torch.bfloat16, device=dev)
                   for name, K, N in LINEARS}
-            row = {}
-            for fn_name, fn in (("bi", bi.gemm), ("fast", bi.gemm_fast)):
-                row[fn_name] = {}
-                for name, K, N in LINEARS:
-                    reps = 4 if Mx >= 1024 else 20
-                    calls = [(ax[name], wsets[i % len(wsets)][name], ox[name]) for i in range(reps)]
-                    row[fn_name][name] = graph_time_us(torch, fn, calls)
+            row = {"bi": {}, "fast": {}}
+            for name, K, N in LINEARS:
+                reps = 4 if Mx >= 1024 else 20
+                calls = [(ax[name], wsets[i % len(wsets)][name], ox[name]) for i in range(reps)]
+                row["bi"][name], row["fast"][name] = paired_graph_time_us(
+                    torch, bi.gemm, bi.gemm_fast, calls)
             lin = {}
             for name, K, N in LINEARS:
                 tb, tf = row["bi"][name], row["fast"][name]
