@@ -72,13 +72,20 @@ __device__ __forceinline__ int sk_phys(int row, int chunk) {  // W: element offs
 __device__ __forceinline__ int sk_xphys(int row, int chunk) {  // x: rows of 64 chunks
   return row * SK_ROWS + ((chunk ^ (row & 15)) << 3);
 }
+__device__ __forceinline__ int sk_xqphys(int row, int chunk) {  // x quarter: rows of 16 chunks
+  return row * SK_QROWS + ((chunk ^ (row & 15)) << 3);
+}
 
+// With 64 rows (MT = 4) the x slab of a whole segment would take 64 KB of
+// LDS, leaving room for one workgroup per CU; it is staged a quarter (128
+// K) at a time instead, beside the W quarter, so that two fit.
 template <int MT>  // 16-row sub-tiles of x: 1, 2 or 4
 __global__ __launch_bounds__(512, MT == 4 ? 2 : 4) void gemm_skinny_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ part,
     int M, int N, int K) {
+  constexpr bool XQ = MT == 4;  // x staged by quarters
   __shared__ __attribute__((aligned(16))) uint16_t wl[SK_QROWS * SK_BN];
-  __shared__ __attribute__((aligned(16))) uint16_t xl[16 * MT * SK_ROWS];
+  __shared__ __attribute__((aligned(16))) uint16_t xl[16 * MT * (XQ ? SK_QROWS : SK_ROWS)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -98,11 +105,21 @@ __global__ __launch_bounds__(512, MT == 4 ? 2 : 4) void gemm_skinny_kernel(
   // x slab: chunk c = tid + 512 i is row c/64, 16-B chunk c%64 of the
   // segment (k past K, within a row, is never multiplied: such K-blocks are
   // skipped below)
+  // (XQ: load 2q + h is quarter q, chunk c = tid + 512 h: row c/16, chunk
+  // 16 q + c%16 of the segment)
   u32x4_t xreg[2 * MT];
 #pragma unroll
   for (int i = 0; i < 2 * MT; ++i) {
-    const int c = tid + 512 * i;
-    const int r = c >> 6, ch = c & 63;
+    int r, ch;
+    if constexpr (XQ) {
+      const int c = tid + 512 * (i & 1);
+      r = c >> 4;
+      ch = 16 * (i >> 1) + (c & 15);
+    } else {
+      const int c = tid + 512 * i;
+      r = c >> 6;
+      ch = c & 63;
+    }
     xreg[i] = bufld128(xr, r < M ? (uint32_t)(r * K + k0 + ch * 8) * 2 : 0x80000000u);
   }
   // W slab: chunk c = tid + 512 i is row c/16, 16-B chunk c%16; loads
@@ -119,10 +136,12 @@ __global__ __launch_bounds__(512, MT == 4 ? 2 : 4) void gemm_skinny_kernel(
       off += RPL * row_bytes;
     }
   }
+  if constexpr (!XQ) {
 #pragma unroll
-  for (int i = 0; i < 2 * MT; ++i) {
-    const int c = tid + 512 * i;
-    *(u32x4_t*)&xl[sk_xphys(c >> 6, c & 63)] = xreg[i];
+    for (int i = 0; i < 2 * MT; ++i) {
+      const int c = tid + 512 * i;
+      *(u32x4_t*)&xl[sk_xphys(c >> 6, c & 63)] = xreg[i];
+    }
   }
 
   // chains: (BN/16) column groups x MT sub-tiles over 8 waves; wave w takes
@@ -149,6 +168,13 @@ __global__ __launch_bounds__(512, MT == 4 ? 2 : 4) void gemm_skinny_kernel(
       const int c = tid + 512 * h;  // row c/16 of the quarter, chunk c%16
       *(u32x4_t*)&wl[sk_phys(c / SK_WCH, c % SK_WCH)] = wreg[LPQ * q + h];
     }
+    if constexpr (XQ) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = tid + 512 * h;
+        *(u32x4_t*)&xl[sk_xqphys(c >> 4, c & 15)] = xreg[2 * q + h];
+      }
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -162,7 +188,9 @@ __global__ __launch_bounds__(512, MT == 4 ? 2 : 4) void gemm_skinny_kernel(
         const u32x4_t bf = u32x4_t{b0.x, b0.y, b1.x, b1.y};
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-          const u32x4_t af = *(const u32x4_t*)&xl[sk_xphys((sub0 + i) * 16 + arow, kb * 4 + g)];
+          const u32x4_t af =
+              XQ ? *(const u32x4_t*)&xl[sk_xqphys((sub0 + i) * 16 + arow, j * 4 + g)]
+                 : *(const u32x4_t*)&xl[sk_xphys((sub0 + i) * 16 + arow, kb * 4 + g)];
           a[i] = mfma16x16x32(af, bf, a[i]);
         }
       }
