@@ -51,7 +51,8 @@ def test_config1_rows_at_m1_equal_rows_at_m8(gpu):
 @pytest.mark.parametrize("M,N,K", [
     (1, 64, 32), (1, 192, 544), (5, 128, 1056), (16, 320, 512), (16, 64, 32), (13, 128, 1536),
     (16, 64, 2080), (17, 64, 96),
-    (64, 192, 1024), (65, 256, 544), (130, 192, 1056), (300, 320, 96)])
+    (64, 192, 1024), (65, 256, 544), (130, 192, 1056), (300, 320, 96),
+    (48, 320, 1056), (33, 128, 608), (40, 64, 96)])
 def test_parity_with_oracle_small_shapes(gpu, M, N, K):
     x, w = synth.gemm_inputs(M, K, N, seed=M + N + K, w_std=0.5)
     y = gpu.gemm(x.to(DEV), w.to(DEV))
