@@ -425,7 +425,8 @@ def bench_rmsnorm(torch, bi, synth, dev, args):
 def bench_verify(torch, bi, synth, dev, args):
     """LLM-42-style grouped verification on the Llama-3-8B-shaped decoder
     (32 layers, random init): 6 requests with prompts of 64..2048 tokens are
-    prefilled in one multi-query pass (timed), then 256 window tokens split
+    prefilled in one multi-query pass (timed; logits of each prompt's last
+    row only), then 256 window tokens split
     over them are verified grouped (timed): rows grouped by request through
     the multi-query attention, and the same rows shuffled through the per-row
     decode attention.  Counts logits that differ between those two, between
@@ -442,22 +443,23 @@ def bench_verify(torch, bi, synth, dev, args):
     dec = Decoder(cfg, w, req.num_pages, 4096, dev)
     segs = [(r, np.arange(n), req.prompts[r]) for r, n in enumerate(req.prompt_lens)]
     pre_rows = dec.prepare(*synth.grouped_rows(req, segs))
-    prompt_logits = dec.run(pre_rows)
+    # logits of each prompt's last row only, as an engine's prefill needs
+    last = np.cumsum(req.prompt_lens) - 1
+    last_d = torch.from_numpy(last.astype(np.int32)).to(dev)
+    prompt_logits = dec.run(pre_rows, logit_rows=last_d)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(3):
-        dec.run(pre_rows)      # rewrites the same K/V bits
+        dec.run(pre_rows, logit_rows=last_d)      # rewrites the same K/V bits
     e1.record()
     torch.cuda.synchronize()
     ms_prefill = e0.elapsed_time(e1) / 3
-    last = np.cumsum(req.prompt_lens) - 1
     pre_mism = 0
     for r in range(len(segs)):
         n = req.prompt_lens[r]
         alone = dec.forward(*req.rows([r], [n - 1], req.prompts[r][-1:]))
-        pre_mism += int((alone.view(torch.int16) !=
-                         prompt_logits[last[r]:last[r] + 1].view(torch.int16)).sum())
+        pre_mism += int((alone.view(torch.int16) != prompt_logits[r:r + 1].view(torch.int16)).sum())
     del prompt_logits
     rng = np.random.default_rng(15)
     win = [(r, req.prompt_lens[r] + i, int(rng.integers(0, cfg.vocab)))

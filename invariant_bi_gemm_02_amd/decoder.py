@@ -58,8 +58,12 @@ class Decoder:
         return (up(tokens), up(positions), up(positions + 1), up(block_table),
                 int(positions.max()) + 1, grouped)
 
-    def run(self, rows) -> torch.Tensor:
-        """Logits [M, vocab] (bf16) for rows from prepare()."""
+    def run(self, rows, logit_rows=None) -> torch.Tensor:
+        """Logits [M, vocab] (bf16) for rows from prepare(); with logit_rows
+        (device int32 row indices) only those rows' logits, in that order
+        (a prefill needs each prompt's last row only).  The rows are gathered
+        with the embedding kernel; every step is row-independent, so their
+        bits are the same either way."""
         cfg, w = self.cfg, self.w
         tok, pos, ctx, bt, max_ctx, grouped = rows
         M = tok.shape[0]
@@ -80,6 +84,8 @@ class Decoder:
             x = bi.rmsnorm(h, w[f"{l}.ffn_norm"], cfg.eps)
             a = bi.silu_mul(bi.gemm(x, w[f"{l}.wgu"]))
             h = bi.add(h, bi.gemm(a, w[f"{l}.wdown"]))
+        if logit_rows is not None:
+            h = bi.embed(logit_rows, h)
         return bi.gemm(bi.rmsnorm(h, w["final_norm"], cfg.eps), w["lm_head"])
 
     def forward(self, tokens, positions, block_table, row_start=None) -> torch.Tensor:

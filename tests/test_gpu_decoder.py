@@ -183,6 +183,23 @@ def test_small_decoder_prefill_one_pass_chunked_and_token_by_token(gpu):
     assert rel.max() <= 2.0 ** -6 and rel.mean() <= 2.0 ** -11, (rel.max(), rel.mean())
 
 
+def test_logits_of_selected_rows_are_those_rows_of_all_logits(gpu):
+    """run(rows, logit_rows=...) gathers the rows before the final norm and
+    LM head (the embedding kernel as a row gather): the logits of the last
+    row of each prompt, in any order, are bitwise those rows of the full
+    logits."""
+    cfg = synth.TINY
+    w = synth.decoder_weights(cfg, seed=18, device=DEV)
+    req = synth.Requests([31, 9, 50], max_len=64, vocab=cfg.vocab, page_size=16, seed=19)
+    segs = [(r, np.arange(n), req.prompts[r]) for r, n in enumerate(req.prompt_lens)]
+    dec = Decoder(cfg, w, req.num_pages, 64)
+    rows = dec.prepare(*synth.grouped_rows(req, segs))
+    full = bits(dec.run(rows))
+    pick = np.array([89, 30, 39, 0], np.int32)   # last rows of prompts 2, 0, 1, and row 0
+    sel = bits(dec.run(rows, logit_rows=dev_i32(pick)))
+    np.testing.assert_array_equal(sel, full[pick])
+
+
 def test_llama3_8b_prefill_is_query_length_invariant(gpu):
     """The Llama-3-8B-shaped decoder: six prompts (1..700 tokens) prefilled
     in one multi-query pass and in 128-row chunks give the same logits;
