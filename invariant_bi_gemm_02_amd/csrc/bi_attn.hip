@@ -698,8 +698,11 @@ int launch_prefill_attn(const uint16_t* q, const uint16_t* kv, const int32_t* bl
   // combines them itself.  Either way every chunk is computed as in the
   // decode entry point and combined in chunk order, so the split never
   // changes the bits.
-  const long long groups =
-      nwg >= 2048 ? 1 : std::max(1LL, std::min((long long)ncs, (8192 + nwg - 1) / nwg));
+  // (the combine kernel's grid has one row of workgroups per query row, at
+  // most 65535)
+  const long long groups = (nwg >= 2048 || d->batch > 65535)
+                               ? 1
+                               : std::max(1LL, std::min((long long)ncs, (8192 + nwg - 1) / nwg));
   const int cpw = (int)((ncs + groups - 1) / groups);
   const long long ngy = (ncs + cpw - 1) / cpw;
   if (ngy > 65535) return BI_ERR_UNSUPPORTED;

@@ -80,7 +80,7 @@ __device__ __forceinline__ int sk_xqphys(int row, int chunk) {  // x quarter: ro
 // LDS, leaving room for one workgroup per CU; it is staged a quarter (128
 // K) at a time instead, beside the W quarter, so that two fit.
 template <int MT>  // 16-row sub-tiles of x: 1, 2 or 4
-__global__ __launch_bounds__(512, MT == 4 ? 2 : 4) void gemm_skinny_kernel(
+__global__ __launch_bounds__(512, 4) void gemm_skinny_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, float* __restrict__ part,
     int M, int N, int K) {
   constexpr bool XQ = MT == 4;  // x staged by quarters
