@@ -567,16 +567,35 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool fast, int num_cus) {
   return (size_t)ceil_div(K, kc) * (size_t)M * (size_t)N * sizeof(float);
 }
 
+// Tile order of the tile kernel (see remap in gemm_tile_kernel).
+static int tile_remap(int64_t tm, int64_t tn) {
+  return (tm % 8 == 0 && tn % 4 == 0) ? 3 : (tn % 8 == 0) ? 2 : ((tm * tn) % 8 == 0) ? 1 : 0;
+}
+
+// The skinny kernel for M <= 64, x padded to 16, 32 or 64 rows: the S
+// segment sums of every 128-column tile into part [S][M][N].
+static int launch_skinny(const uint16_t* x, const uint16_t* W, float* part, int64_t M, int64_t N,
+                         int64_t K, int64_t S, hipStream_t stream) {
+  const dim3 grid((unsigned)ceil_div(N, SK_BN), (unsigned)S);
+  if (M <= 16)
+    hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(512), 0, stream, x, W, part, (int)M,
+                       (int)N, (int)K);
+  else if (M <= 32)
+    hipLaunchKernelGGL(gemm_skinny_kernel<2>, grid, dim3(512), 0, stream, x, W, part, (int)M,
+                       (int)N, (int)K);
+  else
+    hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(512), 0, stream, x, W, part, (int)M,
+                       (int)N, (int)K);
+  return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
 int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, int64_t N,
                 int64_t K, void* ws, size_t ws_bytes, hipStream_t stream, bool fast, int num_cus) {
   const int64_t S = ceil_div(K, BI_KC);
   const GemmPath p = gemm_path(M, N);
   if (p == GemmPath::Tile || p == GemmPath::TileSlice) {
     const int64_t tm = ceil_div(M, TILE_BM), tn = ceil_div(N, TL_BN);
-    const int remap = (tm % 8 == 0 && tn % 4 == 0) ? 3
-                      : (tn % 8 == 0)                 ? 2
-                      : ((tm * tn) % 8 == 0)          ? 1
-                                                      : 0;
+    const int remap = tile_remap(tm, tn);
     if (p == GemmPath::Tile) {
       dim3 grid((unsigned)(tm * tn));
       if (fast)
@@ -607,17 +626,7 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
   if (S > 65535) return BI_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < (size_t)S * (size_t)M * (size_t)N * sizeof(float)) return BI_ERR_WORKSPACE;
   float* part = (float*)ws;
-  const dim3 grid((unsigned)ceil_div(N, SK_BN), (unsigned)S);
-  if (M <= 16)
-    hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(512), 0, stream, x, W, part, (int)M,
-                       (int)N, (int)K);
-  else if (M <= 32)
-    hipLaunchKernelGGL(gemm_skinny_kernel<2>, grid, dim3(512), 0, stream, x, W, part, (int)M,
-                       (int)N, (int)K);
-  else
-    hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(512), 0, stream, x, W, part, (int)M,
-                       (int)N, (int)K);
-  if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
+  if (launch_skinny(x, W, part, M, N, K, S, stream) != BI_OK) return BI_ERR_HIP;
   hipLaunchKernelGGL(gemm_fold_kernel, dim3((unsigned)ceil_div(N, 256), (unsigned)M), dim3(64),
                      0, stream, part, y, (int)M, (int)N, (int)S);
   return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
@@ -631,22 +640,10 @@ int launch_gemm_segments(const uint16_t* x, const uint16_t* W, float* part, int6
                          int64_t K, hipStream_t stream) {
   const int64_t S = ceil_div(K, BI_KC);
   if (S > 65535) return BI_ERR_UNSUPPORTED;
-  if (M <= SKINNY_MAX_M) {
-    const dim3 grid((unsigned)ceil_div(N, SK_BN), (unsigned)S);
-    if (M <= 16)
-      hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(512), 0, stream, x, W, part, (int)M,
-                         (int)N, (int)K);
-    else if (M <= 32)
-      hipLaunchKernelGGL(gemm_skinny_kernel<2>, grid, dim3(512), 0, stream, x, W, part, (int)M,
-                         (int)N, (int)K);
-    else
-      hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(512), 0, stream, x, W, part, (int)M,
-                         (int)N, (int)K);
-    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
-  }
+  if (M <= SKINNY_MAX_M) return launch_skinny(x, W, part, M, N, K, S, stream);
   if (N > SLICE_MAX_N) return BI_ERR_UNSUPPORTED;
   const int64_t tm = ceil_div(M, TILE_BM), tn = ceil_div(N, TL_BN);
-  const int remap = (tn % 8 == 0) ? 2 : ((tm * tn) % 8 == 0) ? 1 : 0;
+  const int remap = tile_remap(tm, tn);
   const int64_t spw = segments_per_slice(tm * tn, S);
   hipLaunchKernelGGL((gemm_tile_kernel<false, true>),
                      dim3((unsigned)(tm * tn), (unsigned)ceil_div(S, spw)), dim3(512), 0, stream,
