@@ -222,10 +222,29 @@ def cpu_baseline(synth, oracle, M, budget_s=12.0):
         for f in futs:
             f.result()
     dt = time.perf_counter() - t0
+    # the same oracle on one core: 4 rows of each linear, in this thread
+    flops1 = 0.0
+    t1 = time.perf_counter()
+    for name, x, w, K, N in jobs:
+        for r in range(4):
+            oracle.gemm(x[r:r + 1], w)
+            flops1 += gemm_flops(1, K, N)
+    dt1 = time.perf_counter() - t1
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{rows_per_linear} rows of each of qkv/o/gate_up/down (one oracle call "
                       f"per row, rows spread over {cores} threads); {dt:.1f} s; rows are "
-                      f"independent, so per-row cost is that of the M={M} batch"}
+                      f"independent, so per-row cost is that of the M={M} batch",
+            "value_1core": flops1 / dt1 / 1e12,
+            "sample_1core": f"4 rows of each linear on one core; {dt1:.1f} s",
+            "cpu_model": model, "host_cpus": os.cpu_count()}
 
 
 def main():
