@@ -537,6 +537,50 @@ def bench_verify(torch, bi, synth, dev, args):
     torch.cuda.synchronize()
     ms_commit = e0.elapsed_time(e1) / reps
     acc, fix = bi.verify_commit(cand, ver, row_start, commit)
+    # a decode step: the first window token of every request, one row each
+    # (per-row decode attention, M = 6 through the skinny GEMMs); each row's
+    # logits must be the same bits as that row in the grouped verify
+    first = [int(np.nonzero((rid == r) & (pos == req.prompt_lens[r]))[0][0])
+             for r in range(len(sizes))]
+    d_rows = dec.prepare(*req.rows(rid[first], pos[first], tok[first]))
+    d_logits = dec.run(d_rows)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dec.run(d_rows)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_decode = e0.elapsed_time(e1) / reps
+    dec_mism = int((d_logits.view(torch.int16) !=
+                    grouped[torch.from_numpy(np.array(first)).to(dev)].view(torch.int16)).sum())
+    # the decode step and the verify step captured in HIP graphs (the forward
+    # is launch-bound at a few rows): every replay, with synchronizations and
+    # eager work between replays, must give the eager logits bit for bit
+    graph_ms, graph_mism = {}, 0
+    for name, rr, ref in (("decode", d_rows, d_logits), ("verify", g_rows, g_logits)):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            dec.run(rr)                       # workspaces of the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            g_out = dec.run(rr)
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            graph_mism += int((g_out.view(torch.int16) != ref.view(torch.int16)).sum())
+            dec.run(rr)                       # eager work between replays
+            torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms[name] = e0.elapsed_time(e1) / reps
+        del graph, g_out
+    del d_logits
     mism, tok_mism = 0, 0
     for r in range(len(sizes)):
         sel = np.nonzero(rid == r)[0]
@@ -557,6 +601,12 @@ def bench_verify(torch, bi, synth, dev, args):
            "ms_per_verify_shuffled_rows_decode_attention": timing["rows"],
            "logit_mismatches_multiquery_vs_shuffled_decode_rows": cross_mism,
            "ms_sample_and_commit": ms_commit,
+           "ms_per_decode_step_6_requests": ms_decode,
+           "logit_mismatches_decode_step_vs_verify_rows": dec_mism,
+           "graph_ms_per_decode_step_6_requests": graph_ms["decode"],
+           "graph_ms_per_verify": graph_ms["verify"],
+           "graph_tokens_per_s": len(win) / (graph_ms["verify"] * 1e-3),
+           "logit_mismatches_graph_replays_vs_eager": graph_mism,
            "sampled_token_mismatches_grouped_vs_alone": tok_mism,
            "accepted_per_request": [int(v) for v in acc.cpu()],
            "committed_lens": [int(v) for v in commit.cpu()]}
