@@ -32,7 +32,7 @@ def sharded(gpu, x, W, seg_counts):
     return gpu.gemm_fold(torch.cat(parts, 0).contiguous())
 
 
-@pytest.mark.parametrize("M", [1, 16, 40, 200, 1024])
+@pytest.mark.parametrize("M", [1, 16, 40, 200, 1024, 2048])
 def test_row_parallel_equals_unsharded(gpu, M):
     x, W = synth.gemm_inputs(M, 4096, 4096, seed=M, w_std=0.02, device=DEV)
     full = gpu.gemm(x, W)
