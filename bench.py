@@ -376,6 +376,7 @@ def main():
         extras["sample_us"] = bench_sample(torch, bi, synth, dev, args)
         extras["prefill_attention"] = bench_prefill_attn(torch, bi, synth, dev, args)
         extras["verify"] = bench_verify(torch, bi, synth, dev, args)
+        extras["decode_batch"] = bench_decode_batch(torch, bi, synth, dev, args)
         extras["ceilings"] = bench_ceilings(torch, synth, dev, M)
         result["extras"] = extras
 
@@ -383,6 +384,81 @@ def main():
         import oracle
         result["cpu_baseline"] = cpu_baseline(synth, oracle, M)
     print(json.dumps(result))
+
+
+def bench_decode_batch(torch, bi, synth, dev, args):
+    """Batch invariance of the whole model in the decode regime: 64 requests
+    with prompts of 64..2048 tokens are prefilled (8 at a time), then one
+    decode step runs all 64 (one row each, per-row attention, M = 64 through
+    the skinny GEMMs).  Eight of the requests decoded alone (batch 1) must
+    give their rows' logits bit for bit.  The step is timed eagerly and from
+    a HIP graph (every checked replay equal to the eager logits)."""
+    import numpy as np
+    from invariant_bi_gemm_02_amd.decoder import Decoder
+    cfg = synth.LLAMA3_8B
+    w = synth.decoder_weights(cfg, seed=21, device=dev)
+    B = 64
+    lens = np.random.default_rng(22).integers(64, 2049, B)
+    req = synth.Requests(lens, max_len=int(lens.max()) + 1, vocab=cfg.vocab,
+                         page_size=cfg.page_size, seed=23)
+    dec = Decoder(cfg, w, req.num_pages, 4096, dev)
+    for g0 in range(0, B, 8):
+        segs = [(r, np.arange(req.prompt_lens[r]), req.prompts[r]) for r in range(g0, g0 + 8)]
+        rows = dec.prepare(*synth.grouped_rows(req, segs))
+        dec.run(rows, logit_rows=torch.zeros(1, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    tok = np.random.default_rng(24).integers(0, cfg.vocab, B).astype(np.int32)
+    rid = np.arange(B)
+    pos = np.array(req.prompt_lens, np.int32)
+    d_rows = dec.prepare(*req.rows(rid, pos, tok))
+    batch = dec.run(d_rows)
+    torch.cuda.synchronize()
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dec.run(d_rows)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dec.run(d_rows)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g_out = dec.run(d_rows)
+    graph_mism = 0
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        graph_mism += int((g_out.view(torch.int16) != batch.view(torch.int16)).sum())
+        dec.run(d_rows)
+        torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_graph = e0.elapsed_time(e1) / reps
+    del graph, g_out
+    mism = 0
+    alone_ids = [int(r) for r in np.random.default_rng(25).choice(B, 8, replace=False)]
+    for r in alone_ids:
+        alone = dec.forward(*req.rows([r], [pos[r]], [tok[r]]))
+        mism += int((alone.view(torch.int16) != batch[r:r + 1].view(torch.int16)).sum())
+    out = {"config": "Llama-3-8B shape, 32 layers, random init, vocab 128256",
+           "requests": B, "prompt_tokens": int(np.sum(lens)),
+           "ms_per_decode_step": ms, "tokens_per_s": B / (ms * 1e-3),
+           "graph_ms_per_decode_step": ms_graph, "graph_tokens_per_s": B / (ms_graph * 1e-3),
+           "requests_checked_alone": alone_ids,
+           "logit_mismatches_batch64_vs_alone": mism,
+           "logit_mismatches_graph_replays_vs_eager": graph_mism}
+    del dec, w, batch
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_ceilings(torch, synth, dev, M):
