@@ -106,9 +106,12 @@ def test_bits_under_concurrent_memory_load(gpu):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("M", [1, 2048])
-def test_gemm_hundred_repeats(gpu, M):
-    x, w = synth.gemm_inputs(M, 4096, 6144, seed=36, device=DEV)
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 6144), (2048, 4096, 6144), (256, 14336, 4096)])
+def test_gemm_hundred_repeats(gpu, M, K, N):
+    """Bitwise stable over 100 calls: the skinny path, the tile path, and the
+    K-slice path with runs of four segments per workgroup (down at M = 256),
+    whose segment-sum stores go out while the load ring keeps running."""
+    x, w = synth.gemm_inputs(M, K, N, seed=36, device=DEV)
     ref = gpu.gemm(x, w)
     outs = [gpu.gemm(x, w) for _ in range(100)]
     torch.cuda.synchronize()
