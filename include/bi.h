@@ -153,6 +153,17 @@ int bi_rmsnorm(const bi_bf16 *x, const bi_bf16 *g, bi_bf16 *y,
 int bi_rmsnorm_fast(const bi_bf16 *x, const bi_bf16 *g, bi_bf16 *y,
                     int64_t M, int64_t H, float eps, void *stream);
 
+/* Residual add followed by RMSNorm, the pair that closes each half of a
+ * decoder layer, in one pass:
+ *   sum[m,h] = bf16_rne(a[m,h] + b[m,h])          (as bi_add)
+ *   y = bi_rmsnorm(sum, g, eps)                    (the same tree and bits)
+ * a, b, sum, y: [M,H] bf16; sum may be a or b (in-place residual), y must not
+ * alias a, b or sum.  g: [H] bf16.  Requirements as bi_rmsnorm, and
+ * H <= 8192; else BI_ERR_UNSUPPORTED.  No workspace. */
+int bi_add_rmsnorm(const bi_bf16 *a, const bi_bf16 *b, const bi_bf16 *g,
+                   bi_bf16 *sum, bi_bf16 *y, int64_t M, int64_t H, float eps,
+                   void *stream);
+
 /* ------------------------------------------------------------------------
  * Paged decode attention (one query token per request, GQA):
  *   out[b,h,:] = softmax_t( scale * q[b,h,:] . k_t ) . v_t,  t < ctx_lens[b],

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     gemm_fast_workspace_bytes,
     rmsnorm,
     rmsnorm_fast,
+    add_rmsnorm,
     paged_decode_attn,
     paged_decode_attn_fast,
     attn_workspace_bytes,

@@ -39,7 +39,7 @@ EXPORTS = ("bi_version", "bi_status_string", "bi_gemm_workspace_bytes", "bi_gemm
            "bi_paged_decode_attn_fast", "bi_embed", "bi_rope_table", "bi_rope", "bi_kv_append",
            "bi_silu_mul", "bi_add", "bi_paged_prefill_attn",
            "bi_gemm_segments", "bi_gemm_fold", "bi_sample", "bi_verify_commit",
-           "bi_sample_workspace_bytes")
+           "bi_sample_workspace_bytes", "bi_add_rmsnorm")
 
 _lock = threading.Lock()
 _lib = None
@@ -71,6 +71,8 @@ def load(path: str | None = None):
         for f in ("bi_rmsnorm", "bi_rmsnorm_fast"):
             getattr(lib, f).restype = ctypes.c_int
             getattr(lib, f).argtypes = [vp, vp, vp, i64, i64, ctypes.c_float, vp]
+        lib.bi_add_rmsnorm.restype = ctypes.c_int
+        lib.bi_add_rmsnorm.argtypes = [vp, vp, vp, vp, vp, i64, i64, ctypes.c_float, vp]
         for f in ("bi_attn_workspace_bytes", "bi_attn_fast_workspace_bytes"):
             getattr(lib, f).restype = sz
             getattr(lib, f).argtypes = [ctypes.POINTER(AttnDesc)]
@@ -217,6 +219,30 @@ def rmsnorm(x, g, eps: float = 1e-5, out=None):
 
 def rmsnorm_fast(x, g, eps: float = 1e-5, out=None):
     return _rmsnorm("bi_rmsnorm_fast", x, g, eps, out)
+
+
+def add_rmsnorm(a, b, g, eps: float = 1e-5, sum_out=None, out=None):
+    """(sum, y): sum = a + b in bf16 (as add), y = rmsnorm(sum, g) (the same
+    bits as the two calls).  sum_out may be a or b (in-place residual)."""
+    lib = load()
+    _check_bf16(a, "a", 2)
+    _check_bf16(b, "b", 2)
+    _check_bf16(g, "g", 1)
+    M, H = a.shape
+    if tuple(b.shape) != (M, H) or g.shape[0] != H:
+        raise ValueError("a, b must be [M,H] and the gain [H]")
+    if sum_out is None:
+        sum_out = torch.empty_like(a)
+    if out is None:
+        out = torch.empty_like(a)
+    for t, name in ((sum_out, "sum_out"), (out, "out")):
+        _check_bf16(t, name, 2)
+        if tuple(t.shape) != (M, H):
+            raise ValueError(f"{name} has the wrong shape")
+    st = lib.bi_add_rmsnorm(a.data_ptr(), b.data_ptr(), g.data_ptr(), sum_out.data_ptr(),
+                            out.data_ptr(), M, H, ctypes.c_float(eps), _stream(a.device))
+    _raise(st, "bi_add_rmsnorm")
+    return sum_out, out
 
 
 def _attn_desc(q, kv, block_table, max_ctx_len, scale, table_rows=None):

@@ -195,6 +195,15 @@ int bi_rmsnorm_fast(const bi_bf16* x, const bi_bf16* g, bi_bf16* y, int64_t M, i
   return bi::launch_rmsnorm(x, g, y, M, H, eps, (hipStream_t)stream, true);
 }
 
+int bi_add_rmsnorm(const bi_bf16* a, const bi_bf16* b, const bi_bf16* g, bi_bf16* sum,
+                   bi_bf16* y, int64_t M, int64_t H, float eps, void* stream) {
+  if (!a || !b || !sum) return BI_ERR_NULL;
+  int st = check_rms(a, g, y, M, H);
+  if (st != BI_OK) return st;
+  if (!aligned16(b) || !aligned16(sum)) return BI_ERR_UNSUPPORTED;
+  return bi::launch_add_rmsnorm(a, b, g, sum, y, M, H, eps, (hipStream_t)stream);
+}
+
 size_t bi_attn_workspace_bytes(const bi_attn_desc* d) {
   if (!d || d->batch <= 0 || d->num_q_heads <= 0 || d->max_ctx_len <= 0) return 0;
   return bi::attn_ws_bytes(d, false, 0);

@@ -19,6 +19,8 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
 // RMSNorm (bi_rmsnorm.hip)
 int launch_rmsnorm(const uint16_t* x, const uint16_t* g, uint16_t* y, int64_t M, int64_t H,
                    float eps, hipStream_t stream, bool fast);
+int launch_add_rmsnorm(const uint16_t* a, const uint16_t* b, const uint16_t* g, uint16_t* sum,
+                       uint16_t* y, int64_t M, int64_t H, float eps, hipStream_t stream);
 
 // Paged decode attention (bi_attn.hip)
 size_t attn_ws_bytes(const bi_attn_desc* d, bool fast, int num_cus);

@@ -86,6 +86,55 @@ __global__ __launch_bounds__(256) void rmsnorm_row_per_wave_kernel(
     stg128(yr + base, scale8(ldg128(xr + base), ldg128(g + base), r));
 }
 
+// Residual add and the RMSNorm that follows it, in one pass over the row:
+// sum = bf16(a + b) (the residual add's arithmetic), then y = RMSNorm(sum)
+// with the tree above, reading the bf16 sums from registers.  The same bits
+// as the two calls.  grid = M, block = 256; H <= 8 * 256 * ADD_RMS_CHUNKS.
+// A lane reads each of its chunks of a and b before writing that chunk of
+// sum, so sum may be a or b.
+static constexpr int ADD_RMS_CHUNKS = 4;
+__global__ __launch_bounds__(256) void add_rmsnorm_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, const uint16_t* __restrict__ g,
+    uint16_t* sum, uint16_t* __restrict__ y, int H, float eps) {
+  __shared__ float wsum[4];
+  const int t = threadIdx.x;
+  const size_t row = (size_t)blockIdx.x * H;
+  u32x4_t s8[ADD_RMS_CHUNKS];
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < ADD_RMS_CHUNKS; ++i) {
+    const int base = 8 * (t + 256 * i);
+    if (base < H) {
+      const u32x4_t a8 = ldg128(a + row + base);
+      const u32x4_t b8 = ldg128(b + row + base);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        s8[i][w] = pack_bf16x2(bf16_lo(a8[w]) + bf16_lo(b8[w]), bf16_hi(a8[w]) + bf16_hi(b8[w]));
+      stg128(sum + row + base, s8[i]);
+      acc = sumsq8(s8[i], acc);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o, 64);
+  if ((t & 63) == 0) wsum[t >> 6] = acc;
+  __syncthreads();
+  const float ss = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  const float r = inv_rms(ss, H, eps);
+#pragma unroll
+  for (int i = 0; i < ADD_RMS_CHUNKS; ++i) {
+    const int base = 8 * (t + 256 * i);
+    if (base < H) stg128(y + row + base, scale8(s8[i], ldg128(g + base), r));
+  }
+}
+
+int launch_add_rmsnorm(const uint16_t* a, const uint16_t* b, const uint16_t* g, uint16_t* sum,
+                       uint16_t* y, int64_t M, int64_t H, float eps, hipStream_t stream) {
+  if (H > 8 * 256 * ADD_RMS_CHUNKS) return BI_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(add_rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, stream, a, b, g, sum, y,
+                     (int)H, eps);
+  return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
 int launch_rmsnorm(const uint16_t* x, const uint16_t* g, uint16_t* y, int64_t M, int64_t H,
                    float eps, hipStream_t stream, bool fast) {
   if (fast && M >= 1024) {

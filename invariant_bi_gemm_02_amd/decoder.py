@@ -1,9 +1,9 @@
 """A Llama-style decoder forward assembled from the library's calls.
 
 Orchestration only: every arithmetic step is one of the C-ABI calls (the
-batch-invariant GEMM, RMSNorm and paged decode attention, and the
-element-wise embedding, RoPE, KV append, SiLU product and residual add), run
-on torch's current stream; torch supplies buffers.  Each row of a forward is
+batch-invariant GEMM, RMSNorm (fused with the residual add before it) and
+paged decode attention, and the element-wise embedding, RoPE, KV append and
+SiLU product), run on torch's current stream; torch supplies buffers.  Each row of a forward is
 one token of some request at some position, attending to its request's KV
 cache up to and including itself, so a batch may mix any number of requests
 and window lengths -- the LLM-42 digest's grouped verification, where the
@@ -61,16 +61,16 @@ class Decoder:
     def run(self, rows, logit_rows=None) -> torch.Tensor:
         """Logits [M, vocab] (bf16) for rows from prepare(); with logit_rows
         (device int32 row indices) only those rows' logits, in that order
-        (a prefill needs each prompt's last row only).  The rows are gathered
-        with the embedding kernel; every step is row-independent, so their
-        bits are the same either way."""
+        (a prefill needs each prompt's last row only).  The normalized rows
+        are gathered with the embedding kernel; every step is row-independent,
+        so their bits are the same either way."""
         cfg, w = self.cfg, self.w
         tok, pos, ctx, bt, max_ctx, grouped = rows
         M = tok.shape[0]
         qd, kd = cfg.q_heads * cfg.head_dim, cfg.kv_heads * cfg.head_dim
         h = bi.embed(tok, w["embed"])
+        x = bi.rmsnorm(h, w["0.attn_norm"], cfg.eps)
         for l in range(cfg.layers):
-            x = bi.rmsnorm(h, w[f"{l}.attn_norm"], cfg.eps)
             qkv = bi.gemm(x, w[f"{l}.wqkv"])
             q = bi.rope(qkv[:, :qd], cfg.q_heads, pos, self.cos, self.sin)
             k = bi.rope(qkv[:, qd:qd + kd], cfg.kv_heads, pos, self.cos, self.sin)
@@ -80,13 +80,16 @@ class Decoder:
             else:
                 att = bi.paged_prefill_attn(q, self.kv[l], grouped[0], grouped[1], ctx,
                                             grouped[2], max_ctx_len=max_ctx)
-            h = bi.add(h, bi.gemm(att.view(M, qd), w[f"{l}.wo"]))
-            x = bi.rmsnorm(h, w[f"{l}.ffn_norm"], cfg.eps)
+            # each residual add and the norm after it in one call (the same
+            # bits as bi.add then bi.rmsnorm); the sum replaces h in place
+            h, x = bi.add_rmsnorm(h, bi.gemm(att.view(M, qd), w[f"{l}.wo"]),
+                                  w[f"{l}.ffn_norm"], cfg.eps, sum_out=h)
             a = bi.silu_mul(bi.gemm(x, w[f"{l}.wgu"]))
-            h = bi.add(h, bi.gemm(a, w[f"{l}.wdown"]))
+            nxt = w[f"{l + 1}.attn_norm"] if l + 1 < cfg.layers else w["final_norm"]
+            h, x = bi.add_rmsnorm(h, bi.gemm(a, w[f"{l}.wdown"]), nxt, cfg.eps, sum_out=h)
         if logit_rows is not None:
-            h = bi.embed(logit_rows, h)
-        return bi.gemm(bi.rmsnorm(h, w["final_norm"], cfg.eps), w["lm_head"])
+            x = bi.embed(logit_rows, x)
+        return bi.gemm(x, w["lm_head"])
 
     def forward(self, tokens, positions, block_table, row_start=None) -> torch.Tensor:
         """prepare() then run(): logits [M, vocab] for host row arrays."""

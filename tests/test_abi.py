@@ -154,6 +154,13 @@ def test_static_lint_no_float_atomics_or_cu_count_in_invariant_paths():
 def test_layer_step_argument_checks(lib):
     ok = 1 << 20  # a 16-byte aligned non-null address; never dereferenced on error paths
     P = ctypes.c_void_p
+    f = ctypes.c_float(1e-5)
+    assert lib.bi_add_rmsnorm(P(ok), None, P(ok), P(ok), P(ok), 1, 4096, f, None) == -1
+    assert lib.bi_add_rmsnorm(P(ok), P(ok), P(ok), None, P(ok), 1, 4096, f, None) == -1
+    assert lib.bi_add_rmsnorm(P(ok), P(ok), P(ok), P(ok), P(ok), 0, 4096, f, None) == -2
+    assert lib.bi_add_rmsnorm(P(ok), P(ok), P(ok), P(ok), P(ok), 1, 4100, f, None) == -3  # H % 8
+    assert lib.bi_add_rmsnorm(P(ok), P(ok), P(ok), P(ok), P(ok), 1, 8200, f, None) == -3  # H > 8192
+    assert lib.bi_add_rmsnorm(P(ok), P(ok + 2), P(ok), P(ok), P(ok), 1, 4096, f, None) == -3
     assert lib.bi_embed(None, P(ok), P(ok), 1, 10, 64, None) == -1
     assert lib.bi_embed(P(ok), P(ok), P(ok), 0, 10, 64, None) == -2
     assert lib.bi_embed(P(ok), P(ok), P(ok), 1, 10, 60, None) == -3      # H % 8

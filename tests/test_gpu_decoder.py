@@ -77,6 +77,27 @@ def test_silu_mul_and_add_against_oracle(gpu):
     np.testing.assert_array_equal(bits(gpu.add(a, b)), oracle.add(bits(a), bits(b)))
 
 
+@pytest.mark.parametrize("M,H", [(1, 4096), (7, 4096), (256, 4096), (3, 512), (5, 8192)])
+def test_add_rmsnorm_is_add_then_rmsnorm(gpu, M, H):
+    """The fused residual add and RMSNorm give the bits of the two calls, out
+    of place and in place (sum written over a), and equal the oracle's add
+    followed by its RMSNorm (both bit-exact steps)."""
+    a = synth.bf16_normal((M, H), seed=40 + M, device=DEV)
+    b = synth.bf16_normal((M, H), seed=41 + M, std=0.5, device=DEV)
+    g = synth.bf16_normal((H,), seed=42, mean=1.0, std=0.1, device=DEV)
+    s_ref = gpu.add(a, b)
+    y_ref = gpu.rmsnorm(s_ref, g)
+    s, y = gpu.add_rmsnorm(a, b, g)
+    a2 = a.clone()
+    s2, y2 = gpu.add_rmsnorm(a2, b, g, sum_out=a2)
+    torch.cuda.synchronize()
+    for got, want in ((s, s_ref), (y, y_ref), (s2, s_ref), (y2, y_ref), (a2, s_ref)):
+        np.testing.assert_array_equal(bits(got), bits(want))
+    s_or = oracle.add(bits(a), bits(b))
+    np.testing.assert_array_equal(bits(s), s_or)
+    np.testing.assert_array_equal(bits(y), oracle.rmsnorm(s_or, bits(g)))
+
+
 def _prefill_and_window(req, seed, window):
     """Rows of every prompt, then a verify window (per-request sizes)."""
     pre = [(r, p, t) for r in range(len(req.prompts)) for p, t in enumerate(req.prompts[r])]
