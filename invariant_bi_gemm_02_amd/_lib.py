@@ -108,7 +108,14 @@ def version() -> str:
 
 
 class Workspace:
-    """A device scratch buffer that grows on demand (one per stream)."""
+    """A device scratch buffer that grows on demand (one per stream).
+
+    Under HIP graph capture every call gets a buffer of its own instead: the
+    captured kernels keep its address for every replay, so it must belong to
+    the graph's memory pool, which lives as long as the graph.  A cached
+    buffer would not: a later, larger call frees it, and once its pool is
+    released (torch empties the cache before each capture) the replays would
+    write to unmapped memory."""
 
     def __init__(self, device=None):
         self.device = torch.device(device or "cuda")
@@ -116,6 +123,8 @@ class Workspace:
 
     def get(self, nbytes: int) -> torch.Tensor:
         nbytes = max(int(nbytes), 256)
+        if torch.cuda.is_current_stream_capturing():
+            return torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         if self.buf is None or self.buf.numel() < nbytes:
             self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return self.buf
