@@ -34,7 +34,11 @@
  *     matching *_workspace_bytes query (0 means ws may be NULL).  It is
  *     scratch: its contents need no initialisation and are undefined after
  *     the call.  One workspace may be reused by any sequence of calls on one
- *     stream; concurrent calls must use distinct workspaces.
+ *     stream; concurrent calls must use distinct workspaces.  A call captured
+ *     into a HIP graph keeps its pointers, the workspace's included, for
+ *     every replay: the workspace must stay allocated while the graph may be
+ *     replayed, and work that uses it between replays must be ordered with
+ *     them on the same stream.
  *   - No global mutable state: concurrent calls on different streams with
  *     distinct workspaces are safe.
  *   - Determinism contract (bi_* entry points, not the _fast twins): the
