@@ -25,6 +25,12 @@ schedule oracle.  Parity status per function:
                      softmax, temperature limits); its logarithms are the
                      platform's, so near-ties are unpinned.
 * ``verify_commit``  pinned by worked cases of the commit-or-rollback rule.
+* ``decoder.OracleDecoder`` (the stacked forward) pinned: reductions with
+                     zeroed branches, row independence, the first token's
+                     self-attention, and the whole composition (MLP active,
+                     positions over several pages, a cache read by a later
+                     call) against an independent float64 forward under
+                     bounds that planted mistakes break.
 """
 from __future__ import annotations
 

@@ -39,13 +39,21 @@ class OracleDecoder:
                      self.cos, self.sin)
             v = qkv[:, qd + kd:].reshape(M, cfg.kv_heads, D)
             cache = self.kv[l]
-            for m in range(M):
-                page = bt[m, pos[m] // PS]
-                cache[page, 0, :, pos[m] % PS, :] = k[m]
-                cache[page, 1, :, pos[m] % PS, :] = v[m]
+            self.write_kv(cache, bt, pos, k, v)
             att = paged_decode_attn(q, cache, bt, pos + 1, num_kv_heads=cfg.kv_heads,
                                     page_size=PS)
             h = add(h, gemm(att.reshape(M, qd), w[f"{l}.wo"]))
             x = rmsnorm(h, w[f"{l}.ffn_norm"], cfg.eps)
             h = add(h, gemm(silu_mul(gemm(x, w[f"{l}.wgu"])), w[f"{l}.wdown"]))
         return gemm(rmsnorm(h, w["final_norm"], cfg.eps), w["lm_head"])
+
+    def write_kv(self, cache, bt, pos, k, v):
+        """Row m's key and value heads go to slot pos % page_size of page
+        block_table[m][pos / page_size] (the paged layout the attention
+        reads: token t of a request sits in page t / page_size, slot
+        t % page_size)."""
+        PS = self.cfg.page_size
+        for m in range(len(pos)):
+            page = bt[m, pos[m] // PS]
+            cache[page, 0, :, pos[m] % PS, :] = k[m]
+            cache[page, 1, :, pos[m] % PS, :] = v[m]

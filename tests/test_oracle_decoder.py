@@ -1,7 +1,11 @@
 """Pins for the oracle's decoder forward: with the attention and MLP outputs
 zeroed the stack reduces to embedding -> final norm -> LM head, computed
 here from the separately pinned steps; rows give the same bits alone and
-grouped; a single token at position 0 attends to itself only."""
+grouped; a single token at position 0 attends to itself only; and the whole
+composition (MLP active, positions 0..45 over several shuffled pages, a
+second call reading the cache the first wrote) agrees with an independent
+float64 forward under bounds derived from the bf16 storage, which three
+mistakes planted in the oracle break."""
 import numpy as np
 import pytest
 
@@ -68,3 +72,183 @@ def test_first_token_attends_to_itself(weights):
     h1 = oracle.add(h, oracle.gemm(att, w["0.wo"]))
     want = oracle.gemm(oracle.rmsnorm(h1, w["final_norm"], cfg.eps), w["lm_head"])
     np.testing.assert_array_equal(logits, want)
+
+
+# ---------------------------------------------------------------------------
+# The whole composition against an independent fp64 forward
+# ---------------------------------------------------------------------------
+# A Llama decoder written out from its textbook definition in numpy float64:
+# RMSNorm, the fused q|k|v projection, rotate-half RoPE with angle
+# p * theta^(-2i/D) for the pair (i, i + D/2), causal GQA softmax attention
+# over a per-request list of cached keys and values (no pages), the output
+# projection, the residual adds, SiLU(gate) * up with the up projection laid
+# out [gate | up], the down projection, the final norm and the LM head.  The
+# tensors a layer hands from step to step are bf16, so every step's fp64
+# result is rounded to bf16 (round to nearest even) where the method stores
+# it.  Nothing here calls the oracle.
+import torch  # noqa: E402
+
+PIN_CFG = synth.DecoderConfig(layers=2, hidden=512, q_heads=4, kv_heads=2, ffn=768, vocab=640)
+
+
+def _bf(a):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    return t.to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class Fp64Decoder:
+    def __init__(self, cfg, weight_bits):
+        self.cfg = cfg
+        self.w = {k: _f64(v) for k, v in weight_bits.items()}
+        self.cache = {}          # (layer, request, position) -> (k [Hkv, D], v [Hkv, D])
+
+    def _norm(self, h, g):
+        r = 1.0 / np.sqrt(np.mean(h * h, axis=1, keepdims=True) + self.cfg.eps)
+        return _bf(h * r * g)
+
+    def _rope(self, x, pos):
+        D = self.cfg.head_dim
+        i = np.arange(D // 2, dtype=np.float64)
+        ang = pos[:, None].astype(np.float64) * self.cfg.theta ** (-2.0 * i / D)
+        c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+        a, b = x[..., :D // 2], x[..., D // 2:]
+        return _bf(np.concatenate([a * c - b * s, b * c + a * s], axis=-1))
+
+    def forward(self, req_ids, positions, tokens):
+        cfg, w = self.cfg, self.w
+        D, Hq, Hkv = cfg.head_dim, cfg.q_heads, cfg.kv_heads
+        G = Hq // Hkv
+        pos = np.asarray(positions)
+        M = len(pos)
+        h = w["embed"][np.asarray(tokens)]
+        for l in range(cfg.layers):
+            qkv = _bf(self._norm(h, w[f"{l}.attn_norm"]) @ w[f"{l}.wqkv"])
+            q = self._rope(qkv[:, :Hq * D].reshape(M, Hq, D), pos)
+            k = self._rope(qkv[:, Hq * D:(Hq + Hkv) * D].reshape(M, Hkv, D), pos)
+            v = qkv[:, (Hq + Hkv) * D:].reshape(M, Hkv, D)
+            for m in range(M):
+                self.cache[(l, int(req_ids[m]), int(pos[m]))] = (k[m], v[m])
+            att = np.empty((M, Hq, D))
+            for m in range(M):
+                keys = np.stack([self.cache[(l, int(req_ids[m]), t)][0] for t in range(pos[m] + 1)])
+                vals = np.stack([self.cache[(l, int(req_ids[m]), t)][1] for t in range(pos[m] + 1)])
+                for hh in range(Hq):
+                    s = keys[:, hh // G, :] @ q[m, hh] / np.sqrt(D)
+                    p = np.exp(s - s.max())
+                    att[m, hh] = p @ vals[:, hh // G, :] / p.sum()
+            h = _bf(h + _bf(_bf(att.reshape(M, Hq * D)) @ w[f"{l}.wo"]))
+            gu = _bf(self._norm(h, w[f"{l}.ffn_norm"]) @ w[f"{l}.wgu"])
+            g, u = gu[:, :cfg.ffn], gu[:, cfg.ffn:]
+            act = _bf(g / (1.0 + np.exp(-g)) * u)
+            h = _bf(h + _bf(act @ w[f"{l}.wdown"]))
+        return _bf(self._norm(h, w["final_norm"]) @ w["lm_head"])
+
+
+def _pin_weights(cfg, seed):
+    """Random bf16 weights scaled 1/sqrt(fan_in), so that the attention and
+    MLP branches move the residual stream as much as the embedding does (a
+    mistake in either branch then shows in every logit)."""
+    H, F, V = cfg.hidden, cfg.ffn, cfg.vocab
+    qd = cfg.q_heads * cfg.head_dim
+    shapes = {"embed": ((V, H), 1.0), "lm_head": ((H, V), H ** -0.5)}
+    for l in range(cfg.layers):
+        shapes[f"{l}.wqkv"] = ((H, cfg.qkv_width), H ** -0.5)
+        shapes[f"{l}.wo"] = ((qd, H), qd ** -0.5)
+        shapes[f"{l}.wgu"] = ((H, 2 * F), H ** -0.5)
+        shapes[f"{l}.wdown"] = ((F, H), 2.0 * F ** -0.5)
+    w = {k: synth.to_bits(synth.bf16_normal(s, seed + i, std=sd))
+         for i, (k, (s, sd)) in enumerate(sorted(shapes.items()))}
+    for i, k in enumerate(["final_norm"] + [f"{l}.{n}" for l in range(cfg.layers)
+                                            for n in ("attn_norm", "ffn_norm")]):
+        w[k] = synth.to_bits(synth.bf16_normal((H,), seed + 100 + i, mean=1.0, std=0.1))
+    return w
+
+
+def _pin_run(dec_factory):
+    """Two requests across several pages (shuffled page pool): a prefill of
+    positions 0..40 and 0..22 in one call, then a shuffled window of later
+    positions of both in a second call that reads the cached keys/values.
+    Returns the logits of both calls from the decoder under test and from the
+    fp64 forward."""
+    cfg = PIN_CFG
+    w = _pin_weights(cfg, 40)
+    req = synth.Requests([41, 23], max_len=64, vocab=cfg.vocab, page_size=cfg.page_size, seed=41)
+    rng = np.random.default_rng(42)
+    pre = [(r, p, int(req.prompts[r][p])) for r in range(2) for p in range(req.prompt_lens[r])]
+    win = [(r, req.prompt_lens[r] + i, int(rng.integers(0, cfg.vocab)))
+           for r, n in ((0, 5), (1, 3)) for i in range(n)]
+    win = [win[i] for i in rng.permutation(len(win))]
+    dec = dec_factory(cfg, w, req.num_pages)
+    ref = Fp64Decoder(cfg, w)
+    got, want = [], []
+    for rows in (pre, win):
+        rid, pos, tok = map(np.array, zip(*rows))
+        got.append(_f64(dec.forward(*req.rows(rid, pos, tok))))
+        want.append(ref.forward(rid, pos, tok))
+    return np.concatenate(got), np.concatenate(want)
+
+
+# Per logits row: every step evaluates in fp32 where the fp64 forward
+# evaluates exactly, a difference far below half a bf16 ulp of the stored
+# value, so the two agree on a stored bf16 value unless it lies within that
+# difference of a rounding boundary; it then differs by one bf16 ulp.  Once
+# such a value sits in the KV cache or the residual stream, every later
+# stored tensor of that row (and of later positions of the request, through
+# attention) carries a small perturbation, and the fraction of its values
+# near a boundary flip by one ulp too.  So the logits of the affected rows
+# differ by about one bf16 ulp of their own size in a fraction of their
+# elements: at most a few ulps of the row's largest logit (bound: 4 ulp =
+# 2^-6 of the row maximum) and on average at most one ulp of it (2^-8).
+# Measured on this workload: at most 0.0061 and 0.0012 of the row maximum;
+# each planted mistake below exceeds a bound by 3x to 50x.
+MAX_REL = 2.0 ** -6
+MEAN_REL = 2.0 ** -8
+
+
+def _violations(got, want):
+    rowmax = np.max(np.abs(want), axis=1)
+    d = np.abs(got - want)
+    return (np.max(d, axis=1) > MAX_REL * rowmax).sum() + \
+        (np.mean(d, axis=1) > MEAN_REL * rowmax).sum()
+
+
+def test_forward_matches_fp64_decoder_with_mlp_and_later_positions():
+    got, want = _pin_run(lambda cfg, w, pages: OracleDecoder(cfg, w, pages, 64))
+    assert np.all(np.isfinite(got))
+    assert _violations(got, want) == 0
+
+
+class _KvSlotShifted(OracleDecoder):
+    """Planted: keys and values written to slot pos + 1."""
+
+    def write_kv(self, cache, bt, pos, k, v):
+        super().write_kv(cache, bt, np.asarray(pos) + 1, k, v)
+
+
+@pytest.mark.parametrize("mutant", ["silu_on_up", "q_rope_shifted", "kv_slot_shifted"])
+def test_planted_mistakes_fail_the_fp64_pin(mutant, monkeypatch):
+    """Each mistake is planted in the oracle (on the CPU) and must break the
+    bounds: the SiLU applied to the up half with the gate as the multiplier
+    (the [gate | up] halves read the wrong way round); queries rotated for
+    position p + 1 while keys use p (a shift of both would cancel, since a
+    RoPE score depends only on p - t); keys and values written to slot
+    pos + 1."""
+    import oracle.decoder as od
+    cls = OracleDecoder
+    if mutant == "silu_on_up":
+        real = od.silu_mul
+        F = PIN_CFG.ffn
+        monkeypatch.setattr(od, "silu_mul", lambda gu: real(
+            np.ascontiguousarray(np.concatenate([gu[:, F:], gu[:, :F]], axis=1))))
+    elif mutant == "q_rope_shifted":
+        real = od.rope
+        monkeypatch.setattr(od, "rope", lambda x, pos, heads, D, c, s: real(
+            x, np.asarray(pos) + (heads == PIN_CFG.q_heads), heads, D, c, s))
+    else:
+        cls = _KvSlotShifted
+    got, want = _pin_run(lambda cfg, w, pages: cls(cfg, w, pages, 64))
+    assert _violations(got, want) > 0
