@@ -39,15 +39,30 @@
  *     every replay: the workspace must stay allocated while the graph may be
  *     replayed, and work that uses it between replays must be ordered with
  *     them on the same stream.
- *   - No global mutable state: concurrent calls on different streams with
- *     distinct workspaces are safe.
+ *   - Reentrancy: concurrent calls on different streams with distinct
+ *     workspaces are safe.  The library keeps no state that affects a
+ *     result; it fills two read-only caches on first use, thread-safely: the
+ *     version string and each device's CU count (read only by the _fast
+ *     twins).
  *   - Determinism contract (bi_* entry points, not the _fast twins): the
  *     output bits of a row/request depend only on that row's/request's
  *     inputs, the weights, gain or logical KV contents, the library version
- *     and the gfx target.  Plan choice reads only (N, K), H, or
- *     (D, page size, Hq, Hkv).  ([Article] section 4: the reduction order must
+ *     and the gfx target.  ([Article] section 4: the reduction order must
  *     depend on the data only; [Vosti]: kernel choice independent of engine
  *     state, cached KV bound to its logical token position.)
+ *   - What the plan reads.  The reduction schedule -- which values are
+ *     added, in which order, by which instruction -- is fixed by (N, K), by
+ *     H, or by (D, page size, Hq, Hkv).  How that schedule's fixed pieces
+ *     (16-row matrix-core sub-tiles, 512-row K segments, 256-token chunks)
+ *     are grouped into workgroups and kernels reads the batch as well: M
+ *     picks 16/32/64-row or 256-row workgroup tiles and, where few tiles
+ *     would leave compute units idle, how many consecutive segments one
+ *     workgroup runs.  That grouping moves work between workgroups and
+ *     never changes an output bit; the GPU tests check every M of a
+ *     1..2048 sweep against the M = 2048 rows bit for bit.  This is the
+ *     reading taken of the Article's fixed-tile rule (section 4): what
+ *     must not follow M is the arithmetic each output sees, not the
+ *     launch shape.
  */
 #ifndef BI_H
 #define BI_H
@@ -205,7 +220,9 @@ typedef struct {
     int32_t max_blocks_per_seq;
     int64_t num_pages;
     int32_t max_ctx_len;
-    float scale; /* usually 1/sqrt(head_dim) */
+    float scale; /* > 0: used as given; <= 0 (or -0): the default
+                    1/sqrt(head_dim), computed by the library as the fp32
+                    division 1.0f / sqrtf(head_dim); NaN: BI_ERR_UNSUPPORTED */
 } bi_attn_desc;
 
 size_t bi_attn_workspace_bytes(const bi_attn_desc *d);

@@ -262,8 +262,7 @@ def _attn_desc(q, kv, block_table, max_ctx_len, scale, table_rows=None):
     if block_table.dim() != 2 or block_table.shape[0] != (B if table_rows is None else table_rows):
         raise ValueError("block_table must be [batch, max_blocks]")
     if scale is None:
-        scale = float(torch.tensor(1.0, dtype=torch.float32) /
-                      torch.sqrt(torch.tensor(float(D), dtype=torch.float32)))
+        scale = 0.0          # the library's default, 1/sqrt(head_dim)
     return AttnDesc(B, Hq, Hkv, D, PS, block_table.shape[1], P, int(max_ctx_len), scale)
 
 

@@ -1,7 +1,11 @@
 // bi_api.hip -- the extern "C" entry points declared in include/bi.h:
 // argument checks, workspace sizing, status codes and version string.
 // Every check happens before anything is enqueued.
+#include <math.h>
 #include <stdio.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "bi_internal.h"
 
@@ -17,17 +21,19 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // CU count of the current device, read once per device; only the fast twins
 // use it (the batch-invariant entry points never look at it).
+// The cache entries are atomics: two threads that race on a device's first
+// call both read the same attribute and store the same value.
 int current_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 int check_gemm(const void* x, const void* W, const void* y, int64_t M, int64_t N, int64_t K) {
@@ -69,14 +75,23 @@ int check_attn(const void* q, const void* kv, const void* bt, const void* cl, co
   return BI_OK;
 }
 
+// A copy of the descriptor with the default softmax scale filled in: a
+// scale <= 0 (or -0) selects 1/sqrt(head_dim), the usual attention scale,
+// rounded as fp32 sqrt then fp32 division.
+bi_attn_desc resolved(const bi_attn_desc* d) {
+  bi_attn_desc r = *d;
+  if (r.scale <= 0.f) r.scale = 1.0f / sqrtf((float)r.head_dim);
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* bi_version(void) {
   static char buf[512];
-  static int done = 0;
-  if (!done) {
+  static std::once_flag once;
+  std::call_once(once, [] {
     snprintf(buf, sizeof buf,
              "libbi 0.1.0 git=%s hip=%d.%d target=gfx950 "
              "gemm: mfma_f32_16x16x32_bf16 KB=%d KC=%d fold=left skinny_maxM=64 "
@@ -85,8 +100,7 @@ const char* bi_version(void) {
              "attn: chunk=%d tile=%d qk=mfma16x16x32 combine=chunk-order exp=__expf",
              BI_GIT_SHA, HIP_VERSION_MAJOR, HIP_VERSION_MINOR, bi::SCHED_GEMM_KB, bi::SCHED_GEMM_KC,
              bi::SCHED_RMS_LANES, bi::SCHED_ATTN_CHUNK, bi::SCHED_ATTN_TILE);
-    done = 1;
-  }
+  });
   return buf;
 }
 
@@ -224,7 +238,8 @@ static int attn_entry(const bi_bf16* q, const bi_bf16* kv, const int32_t* bt, co
   const size_t need = bi::attn_ws_bytes(d, fast, cus);
   if (!ws || ws_bytes < need) return BI_ERR_WORKSPACE;
   if (!aligned16(ws)) return BI_ERR_UNSUPPORTED;
-  return bi::launch_attn(q, kv, bt, cl, out, d, ws, ws_bytes, (hipStream_t)stream, fast, cus);
+  const bi_attn_desc dd = resolved(d);
+  return bi::launch_attn(q, kv, bt, cl, out, &dd, ws, ws_bytes, (hipStream_t)stream, fast, cus);
 }
 
 int bi_paged_decode_attn(const bi_bf16* q, const bi_bf16* kv_pages, const int32_t* block_table,
@@ -253,7 +268,8 @@ int bi_paged_prefill_attn(const bi_bf16* q, const bi_bf16* kv_pages, const int32
   const size_t need = bi::attn_ws_bytes(d, false, 0);
   if (!ws || ws_bytes < need) return BI_ERR_WORKSPACE;
   if (!aligned16(ws)) return BI_ERR_UNSUPPORTED;
-  return bi::launch_prefill_attn(q, kv_pages, block_table, row_start, ctx_lens, out, d, requests,
+  const bi_attn_desc dd = resolved(d);
+  return bi::launch_prefill_attn(q, kv_pages, block_table, row_start, ctx_lens, out, &dd, requests,
                                  max_rows_per_request, ws, ws_bytes, (hipStream_t)stream);
 }
 

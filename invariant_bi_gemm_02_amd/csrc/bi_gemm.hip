@@ -8,7 +8,10 @@
 // This is the two-stage deterministic reduction of the Determinism article
 // (section 4): per-slice partial sums written to a fixed workspace and added
 // in the fixed index order, with no float atomics anywhere; the K split is
-// the same whatever M is, and the M tile is padded rather than re-chosen.
+// the same whatever M is.  The arithmetic unit of the schedule is a 16-row
+// matrix-core sub-tile, padded with zero rows past M; how many sub-tiles
+// one workgroup takes (16, 32, 64 or 256 rows) and which kernel runs them
+// follow M, which moves work between workgroups and never changes a bit.
 //
 // Several kernels implement that schedule; which ones run depends on (M, N),
 // and the bits never do (all issue the same matrix-core instruction on the

@@ -91,10 +91,11 @@ __global__ __launch_bounds__(256) void rmsnorm_row_per_wave_kernel(
 // with the tree above, reading the bf16 sums from registers.  The same bits
 // as the two calls.  grid = M, block = 256; H <= 8 * 256 * ADD_RMS_CHUNKS.
 // A lane reads each of its chunks of a and b before writing that chunk of
-// sum, so sum may be a or b.
+// sum, so sum may be a or b: a, b and sum are therefore not restrict
+// pointers (sum may alias either input); g and y alias nothing.
 static constexpr int ADD_RMS_CHUNKS = 4;
 __global__ __launch_bounds__(256) void add_rmsnorm_kernel(
-    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, const uint16_t* __restrict__ g,
+    const uint16_t* a, const uint16_t* b, const uint16_t* __restrict__ g,
     uint16_t* sum, uint16_t* __restrict__ y, int H, float eps) {
   __shared__ float wsum[4];
   const int t = threadIdx.x;

@@ -110,3 +110,35 @@ def test_fast_twin_parity(gpu, B):
     for b in sorted(set([0, B - 1])):
         want = oracle.paged_decode_attn(qb[b:b + 1], kvb, bt[b:b + 1], cl[b:b + 1], HKV, PS)
         check_close_bf16(got[b:b + 1], want, what=f"fast B={B} b={b}")
+
+
+def test_default_scale_through_the_c_abi(gpu):
+    """A descriptor scale <= 0 (or -0) selects 1/sqrt(head_dim), computed in
+    the library: the same bits as passing fp32(1/sqrt(128)) explicitly, and
+    within tolerance of the oracle's default."""
+    import ctypes
+    from invariant_bi_gemm_02_amd import _lib
+    lib = gpu.load()
+    ctx = np.array([300, 17, 1024], np.int32)
+    q, kv, bt, cl = synth.attn_inputs(ctx, seed=77)
+    qd, kvd = q.to(DEV), kv.to(DEV)
+    btd = torch.from_numpy(bt).to(DEV)
+    cld = torch.from_numpy(cl).to(DEV)
+    B = len(ctx)
+    outs = []
+    explicit = float(np.float32(1.0) / np.sqrt(np.float32(128)))
+    for scale in (0.0, -0.0, -1.0, explicit):
+        d = _lib.AttnDesc(B, 32, HKV, 128, PS, bt.shape[1], kv.shape[0], int(ctx.max()), scale)
+        need = lib.bi_attn_workspace_bytes(ctypes.byref(d))
+        ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        out = torch.empty_like(qd)
+        st = lib.bi_paged_decode_attn(qd.data_ptr(), kvd.data_ptr(), btd.data_ptr(),
+                                      cld.data_ptr(), out.data_ptr(), ctypes.byref(d),
+                                      ws.data_ptr(), need, None)
+        assert st == 0
+        torch.cuda.synchronize()
+        outs.append(synth.to_bits(out))
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+    want = oracle.paged_decode_attn(synth.to_bits(q), synth.to_bits(kv), bt, cl, HKV, PS)
+    check_close_bf16(outs[0], want, what="default scale")
