@@ -83,7 +83,9 @@ enum {
     BI_ERR_UNSUPPORTED = -3, /* shape outside what the kernels handle, or a
                                 pointer not 16-byte aligned                   */
     BI_ERR_WORKSPACE = -4,   /* ws is NULL or ws_bytes smaller than needed   */
-    BI_ERR_HIP = -5          /* the HIP launch itself failed                 */
+    BI_ERR_HIP = -5,         /* the HIP launch itself failed                 */
+    BI_ERR_SCRATCH = -6      /* the call needs more scratch than the
+                                library's static array holds (bi_gemm_noalloc) */
 };
 
 /* Library version, gfx target and every schedule constant, as one static
@@ -126,6 +128,26 @@ size_t bi_gemm_fast_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int bi_gemm_fast(const bi_bf16 *x, const bi_bf16 *W, bi_bf16 *y,
                  int64_t M, int64_t N, int64_t K,
                  void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * bi_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same operation, arguments (less the workspace), requirements, schedule
+ * and bits as bi_gemm.  The segment sums that bi_gemm sends through a
+ * workspace go to a static device array of BI_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends; the
+ * call allocates nothing.  A call whose bi_gemm_workspace_bytes(M, N, K)
+ * exceeds that size returns BI_ERR_SCRATCH and enqueues nothing (with the
+ * Llama-3-8B linears it fits every M <= 64, and M up to about 256 on the
+ * 4096-row ones).  Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU, on any streams, race on it and must be ordered by
+ * the caller.  The array needs no initialisation and keeps the last call's
+ * contents.  Its device address is taken on a device's first call, under
+ * a lock.
+ * ---------------------------------------------------------------------- */
+#define BI_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int bi_gemm_noalloc(const bi_bf16 *x, const bi_bf16 *W, bi_bf16 *y,
+                    int64_t M, int64_t N, int64_t K, void *stream);
 
 /* ------------------------------------------------------------------------
  * The two halves of bi_gemm's schedule, for a row-parallel (K-sharded)

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     version,
     gemm,
     gemm_fast,
+    gemm_noalloc,
     gemm_workspace_bytes,
     gemm_fast_workspace_bytes,
     rmsnorm,

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbi.so")
 
 _STATUS = {0: "BI_OK", -1: "BI_ERR_NULL", -2: "BI_ERR_SHAPE", -3: "BI_ERR_UNSUPPORTED",
-           -4: "BI_ERR_WORKSPACE", -5: "BI_ERR_HIP"}
+           -4: "BI_ERR_WORKSPACE", -5: "BI_ERR_HIP", -6: "BI_ERR_SCRATCH"}
 
 
 class BiError(RuntimeError):
@@ -39,7 +39,7 @@ EXPORTS = ("bi_version", "bi_status_string", "bi_gemm_workspace_bytes", "bi_gemm
            "bi_paged_decode_attn_fast", "bi_embed", "bi_rope_table", "bi_rope", "bi_kv_append",
            "bi_silu_mul", "bi_add", "bi_paged_prefill_attn",
            "bi_gemm_segments", "bi_gemm_fold", "bi_sample", "bi_verify_commit",
-           "bi_sample_workspace_bytes", "bi_add_rmsnorm")
+           "bi_sample_workspace_bytes", "bi_add_rmsnorm", "bi_gemm_noalloc")
 
 _lock = threading.Lock()
 _lib = None
@@ -94,6 +94,7 @@ def load(path: str | None = None):
             "bi_sample_workspace_bytes": [i64],
             "bi_verify_commit": [vp, vp, i32, vp, i32, vp, vp, vp, vp],
             "bi_gemm_fold": [vp, vp, i64, i64, i64, vp],
+            "bi_gemm_noalloc": [vp, vp, vp, i64, i64, i64, vp],
         }
         for f, a in sigs.items():
             getattr(lib, f).restype = ctypes.c_int
@@ -190,6 +191,29 @@ def _gemm(fn_name, wsq, x, w, out, ws):
     st = getattr(lib, fn_name)(x.data_ptr(), w.data_ptr(), out.data_ptr(), M, N, K,
                                buf.data_ptr(), buf.numel(), _stream(x.device))
     _raise(st, fn_name)
+    return out
+
+
+def gemm_noalloc(x, w, out=None):
+    """y = x @ W through bi_gemm_noalloc: bi_gemm's bits, with the library's
+    static scratch instead of a workspace (out is allocated here when None;
+    pass it to allocate nothing)."""
+    lib = load()
+    _check_bf16(x, "x", 2)
+    _check_bf16(w, "W", 2)
+    M, K = x.shape
+    K2, N = w.shape
+    if K != K2:
+        raise ValueError(f"x is [M,{K}] but W is [{K2},N]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _check_bf16(out, "out", 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    st = lib.bi_gemm_noalloc(x.data_ptr(), w.data_ptr(), out.data_ptr(), M, N, K,
+                             _stream(x.device))
+    _raise(st, "bi_gemm_noalloc")
     return out
 
 

@@ -86,6 +86,12 @@ bi_attn_desc resolved(const bi_attn_desc* d) {
 
 }  // namespace
 
+namespace bi {
+int check_gemm_args(const void* x, const void* W, const void* y, int64_t M, int64_t N, int64_t K) {
+  return check_gemm(x, W, y, M, N, K);
+}
+}  // namespace bi
+
 extern "C" {
 
 const char* bi_version(void) {
@@ -112,6 +118,7 @@ const char* bi_status_string(int status) {
     case BI_ERR_UNSUPPORTED: return "unsupported shape or alignment";
     case BI_ERR_WORKSPACE: return "workspace too small";
     case BI_ERR_HIP: return "HIP launch failed";
+    case BI_ERR_SCRATCH: return "needs more scratch than the library's static array holds";
     default: return "unknown status";
   }
 }

@@ -10,6 +10,9 @@
 
 namespace bi {
 
+// bi_gemm's argument checks (bi_api.hip): BI_OK or the status bi_gemm returns
+int check_gemm_args(const void* x, const void* W, const void* y, int64_t M, int64_t N, int64_t K);
+
 // GEMM (bi_gemm.hip)
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool fast, int num_cus);
 int64_t fast_split_kc(int64_t M, int64_t N, int64_t K, int num_cus);

@@ -41,8 +41,21 @@ def test_version_names_target_and_schedule(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert lib.bi_status_string(code)
+    assert lib.bi_status_string(-6) != lib.bi_status_string(-99)
+
+
+def test_noalloc_argument_checks(lib):
+    """bi_gemm_noalloc runs bi_gemm's checks, then refuses a call whose
+    workspace would exceed the static scratch, all before touching a device."""
+    ok = 0x1000
+    assert lib.bi_gemm_noalloc(None, P(ok), P(ok), 1, 64, 32, None) == -1
+    assert lib.bi_gemm_noalloc(P(ok), P(ok), P(ok), 0, 64, 32, None) == -2
+    assert lib.bi_gemm_noalloc(P(ok), P(ok), P(ok), 1, 64, 33, None) == -3
+    assert lib.bi_gemm_noalloc(P(ok + 2), P(ok), P(ok), 1, 64, 32, None) == -3
+    assert lib.bi_gemm_workspace_bytes(64, 28672, 14336) > (64 << 20)
+    assert lib.bi_gemm_noalloc(P(ok), P(ok), P(ok), 64, 28672, 14336, None) == -6
 
 
 def P(v):

@@ -1,0 +1,82 @@
+"""bi_gemm_noalloc, the allocation-free GEMM entry point, through the C ABI:
+bitwise bi_gemm's output on two calls in a row, the second with a smaller
+input, on each path that needs scratch (decode-size rows, the K-slice tile
+path) and on the one that needs none; the first call leaves NaN segment sums
+behind, so a read of stale scratch would show; a call that needs more than
+the static array holds is refused with nothing enqueued."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from invariant_bi_gemm_02_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def noalloc(lib, x, w, y):
+    M, K = x.shape
+    N = w.shape[1]
+    return lib.bi_gemm_noalloc(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                               ctypes.c_void_p(y.data_ptr()), M, N, K,
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+
+def bits(t):
+    return t.view(torch.int16)
+
+
+@pytest.mark.parametrize("first,second", [
+    ((64, 28672, 4096), (5, 4096, 14336)),      # skinny path: 56 MiB, then 2.2 MiB
+    ((200, 4096, 4096), (70, 1024, 1536)),      # K-slice tile path
+    ((33, 6144, 4096), (1, 4096, 4096)),        # 32/64-row skinny, then one row
+    ((2048, 4096, 4096), (300, 4096, 4096)),    # full tiles (no scratch), then K-slice
+])
+def test_noalloc_matches_bi_gemm_on_two_calls(gpu, first, second):
+    lib = gpu.load()
+    print(f"noalloc first={first} second={second}", flush=True)
+    for i, (M, N, K) in enumerate((first, second)):
+        x, w = synth.gemm_inputs(M, K, N, seed=500 + i)
+        x, w = x.to(DEV), w.to(DEV)
+        if i == 0:
+            x[M // 2:] = float("nan")        # NaN segment sums stay in the scratch
+        y = torch.full((M, N), 7.0, dtype=torch.bfloat16, device=DEV)
+        assert noalloc(lib, x, w, y) == 0
+        want = gpu.gemm(x, w)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(y), bits(want)), (M, N, K)
+        if i == 1:
+            assert not torch.isnan(y).any()
+
+
+def test_noalloc_refuses_what_does_not_fit(gpu):
+    lib = gpu.load()
+    M, N, K = 64, 28672, 14336                    # 28 segments x 64 x 28672 fp32 = 196 MiB
+    assert lib.bi_gemm_workspace_bytes(M, N, K) > (64 << 20)
+    x = torch.zeros((M, K), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((K, N), dtype=torch.bfloat16, device=DEV)
+    y = torch.full((M, N), 3.0, dtype=torch.bfloat16, device=DEV)
+    assert noalloc(lib, x, w, y) == -6
+    torch.cuda.synchronize()
+    assert bool((y == 3.0).all())                 # nothing was enqueued
+    # and the next call that fits still gives bi_gemm's bits
+    x, w = synth.gemm_inputs(16, 4096, 4096, seed=9)
+    x, w = x.to(DEV), w.to(DEV)
+    y = torch.empty((16, 4096), dtype=torch.bfloat16, device=DEV)
+    assert noalloc(lib, x, w, y) == 0
+    assert torch.equal(bits(y), bits(gpu.gemm(x, w)))
+
+
+def test_noalloc_binding_and_sampled_oracle_rows(gpu):
+    """The Python binding of the same entry point, and rows within the
+    tolerance of the oracle (the bar every bi_gemm path meets)."""
+    import oracle
+    from tolerance import check_close_bf16
+    x, w = synth.gemm_inputs(9, 14336, 4096, seed=21)
+    y = gpu.gemm_noalloc(x.to(DEV), w.to(DEV))
+    torch.cuda.synchronize()
+    xb, wb = synth.to_bits(x), synth.to_bits(w)
+    rows = np.array([0, 4, 8])
+    check_close_bf16(synth.to_bits(y)[rows], oracle.gemm(xb[rows], wb), what="noalloc vs oracle")
