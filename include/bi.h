@@ -412,6 +412,19 @@ int bi_silu_mul(const bi_bf16 *gu, bi_bf16 *out, int64_t M, int64_t F,
 int bi_add(const bi_bf16 *a, const bi_bf16 *b, bi_bf16 *out, int64_t n,
            void *stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement helper (no operation's path uses it): a matrix-core-only loop
+ * that lets a benchmark quote the bf16 rate the chip sustains beside the
+ * published peak.  Each of `workgroups` workgroups of 4 waves runs `iters`
+ * rounds of 8 independent v_mfma_f32_16x16x32_bf16 ops per wave (16384
+ * flops each) on register operands, then writes one float per lane to
+ * out[workgroups * 256] (device memory, 4-byte aligned).  So one call does
+ * workgroups * 4 * iters * 8 * 16384 flops.  1 <= iters <= 2^30,
+ * 1 <= workgroups <= 65535.
+ * ---------------------------------------------------------------------- */
+int bi_ceiling_mfma(float *out, int64_t iters, int64_t workgroups,
+                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     gemm,
     gemm_fast,
     gemm_noalloc,
+    ceiling_mfma,
     gemm_workspace_bytes,
     gemm_fast_workspace_bytes,
     rmsnorm,

@@ -39,7 +39,8 @@ EXPORTS = ("bi_version", "bi_status_string", "bi_gemm_workspace_bytes", "bi_gemm
            "bi_paged_decode_attn_fast", "bi_embed", "bi_rope_table", "bi_rope", "bi_kv_append",
            "bi_silu_mul", "bi_add", "bi_paged_prefill_attn",
            "bi_gemm_segments", "bi_gemm_fold", "bi_sample", "bi_verify_commit",
-           "bi_sample_workspace_bytes", "bi_add_rmsnorm", "bi_gemm_noalloc")
+           "bi_sample_workspace_bytes", "bi_add_rmsnorm", "bi_gemm_noalloc",
+           "bi_ceiling_mfma")
 
 _lock = threading.Lock()
 _lib = None
@@ -95,6 +96,7 @@ def load(path: str | None = None):
             "bi_verify_commit": [vp, vp, i32, vp, i32, vp, vp, vp, vp],
             "bi_gemm_fold": [vp, vp, i64, i64, i64, vp],
             "bi_gemm_noalloc": [vp, vp, vp, i64, i64, i64, vp],
+            "bi_ceiling_mfma": [vp, i64, i64, vp],
         }
         for f, a in sigs.items():
             getattr(lib, f).restype = ctypes.c_int
@@ -192,6 +194,18 @@ def _gemm(fn_name, wsq, x, w, out, ws):
                                buf.data_ptr(), buf.numel(), _stream(x.device))
     _raise(st, fn_name)
     return out
+
+
+def ceiling_mfma(iters: int, workgroups: int, out=None, device=None):
+    """Launch the matrix-core-only loop (a measurement helper); returns the
+    per-lane output tensor and the flops one launch performs."""
+    lib = load()
+    dev = torch.device(device or "cuda")
+    if out is None:
+        out = torch.empty(workgroups * 256, dtype=torch.float32, device=dev)
+    _raise(lib.bi_ceiling_mfma(out.data_ptr(), int(iters), int(workgroups), _stream(dev)),
+           "bi_ceiling_mfma")
+    return out, float(workgroups) * 4 * iters * 8 * 16384
 
 
 def gemm_noalloc(x, w, out=None):

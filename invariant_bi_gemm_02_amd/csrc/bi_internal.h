@@ -62,6 +62,9 @@ int launch_silu_mul(const uint16_t* gu, uint16_t* out, int64_t M, int64_t F,
 int launch_add(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n,
                hipStream_t stream);
 
+// Matrix-core-only loop for measured ceilings (bi_ceiling.hip)
+int launch_mfma_ceiling(float* out, int64_t iters, int64_t workgroups, hipStream_t stream);
+
 // Schedule constants reported by bi_version().
 static constexpr int SCHED_GEMM_KB = 32;
 static constexpr int SCHED_GEMM_KC = 512;
