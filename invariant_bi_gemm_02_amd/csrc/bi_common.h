@@ -56,6 +56,12 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* lds_addr) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
+// The same read from a 32-bit LDS byte address (no generic-pointer cast).
+__device__ __forceinline__ u32x2_t lds_read_tr16_at(uint32_t lds_byte_addr) {
+  i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BI_LDS i16x4_t*)(uintptr_t)lds_byte_addr);
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
 __device__ __forceinline__ u32x4_t ldg128(const void* p) { return *(const u32x4_t*)p; }
 
 // Buffer resource over [base, base + bytes): raw (unswizzled) addressing with
@@ -94,6 +100,22 @@ __device__ __forceinline__ void lds_dma16(i32x4_t rsrc, uint32_t voff, uint32_t 
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "memory");
+}
+
+// The same load with a scalar byte offset added to voff (the buffer's range
+// check applies to voff + soff): a per-stage advance carried in an SGPR
+// leaves the per-lane offsets untouched.
+__device__ __forceinline__ void lds_dma16_so(i32x4_t rsrc, uint32_t voff, uint32_t soff,
+                                             uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
       : "memory");
 }
 

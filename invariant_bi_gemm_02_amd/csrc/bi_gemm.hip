@@ -276,6 +276,25 @@ __global__ __launch_bounds__(64) void gemm_fold_kernel(const float* __restrict__
 // the tile rows, walked in step: each W line is then wanted by two XCDs at
 // about the same time, so one of them finds it in the memory-side cache
 // rather than HBM (remap 2 reads a band's W twice, half a launch apart).
+// Tile index (m fastest: t = column * tm + row) of workgroup `b`.
+__device__ __forceinline__ int tile_of_block(int b, int tm, int tn, int remap) {
+  int t = b;
+  if (remap == 1) {
+    t = (t & 7) * ((tm * tn) >> 3) + (t >> 3);
+  } else if (remap == 3) {
+    const int ncols = tn >> 2, xcd = t & 7, i = t >> 3, pr = xcd & 3, h = xcd >> 2, th = tm >> 1;
+    const int first = (i / (4 * ncols)) * 4, gm = min(4, th - first);
+    const int r = i - first * ncols;
+    t = (pr * ncols + r / gm) * tm + h * th + first + r % gm;
+  } else if (remap == 2) {
+    const int ncols = tn >> 3, xcd = t & 7, i = t >> 3;
+    const int first = (i / (4 * ncols)) * 4, gm = min(4, tm - first);
+    const int r = i - first * ncols;
+    t = (xcd * ncols + r / gm) * tm + first + r % gm;
+  }
+  return t;
+}
+
 static constexpr int TL_BM = 256, TL_BN = 128, TL_BK = 64;
 static constexpr int TL_XS = TL_BM * TL_BK;             // x slab elements (32 KB)
 static constexpr int TL_STAGE = TL_XS + TL_BK * TL_BN;  // + W slab (16 KB)
@@ -300,20 +319,7 @@ __global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
   const int l16 = lane & 15;
   const int tr_r = l16 >> 2, tr_c = lane & 3;
 
-  int t = blockIdx.x;
-  if (remap == 1) {
-    t = (t & 7) * ((tm * tn) >> 3) + (t >> 3);
-  } else if (remap == 3) {
-    const int ncols = tn >> 2, xcd = t & 7, i = t >> 3, pr = xcd & 3, h = xcd >> 2, th = tm >> 1;
-    const int first = (i / (4 * ncols)) * 4, gm = min(4, th - first);
-    const int r = i - first * ncols;
-    t = (pr * ncols + r / gm) * tm + h * th + first + r % gm;
-  } else if (remap == 2) {
-    const int ncols = tn >> 3, xcd = t & 7, i = t >> 3;
-    const int first = (i / (4 * ncols)) * 4, gm = min(4, tm - first);
-    const int r = i - first * ncols;
-    t = (xcd * ncols + r / gm) * tm + first + r % gm;
-  }
+  const int t = tile_of_block(blockIdx.x, tm, tn, remap);
   const int m0 = (t % tm) * TL_BM;
   const int n0 = (t / tm) * TL_BN;
 
@@ -509,6 +515,257 @@ __global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Ring kernel with one K-block per stage: BM x BN tiles of WGM x WGN waves
+// ---------------------------------------------------------------------------
+// The same arithmetic as gemm_tile_kernel (one v_mfma_f32_16x16x32_bf16 per
+// 32-deep K-block, issued as y^T = W^T x^T; with FOLD, segments of 512 from
+// +0 folded left to right in registers) on other tile shapes:
+//   128 x 128, FOLD (4 waves of 64 x 64, two workgroups per CU): the
+//     invariant schedule where 256 x 128 tiles would leave CUs idle but
+//     128 x 128 tiles fill the chip (e.g. o and down at M = 1024), so every
+//     segment stays in registers instead of going through the workspace;
+//   256 x 256, one chain over all of K (8 waves of 64 x 128): the fast
+//     twin's large-M tile, half the L2 bytes per flop of 256 x 128.  The
+//     invariant schedule cannot use it: the fold's running total doubles the
+//     accumulator registers, which at 256 x 256 exceed the register file.
+// The ring holds NS stages of one K-block each (x slab BM rows x 64 B, W slab
+// 32 rows x BN*2 B) filled by direct-to-LDS loads NS - 1 stages ahead, one
+// barrier per stage.  One set of fragments: each W fragment of the first
+// half of the columns is reloaded with the next stage's once that half has
+// issued, each x fragment once its row has, the second half's W fragments at
+// the end of the stage.
+//
+// LDS swizzles (16-byte chunks, XOR of the chunk index with row bits), so
+// that every read of a fragment touches each bank once:
+//   x: rows of 4 chunks; chunk ^ ((row >> 2) & 3) -- a 16-lane read of one
+//      chunk of 16 consecutive rows covers all banks;
+//   W: rows of BN/8 chunks; the transpose read of 8 k-rows x 2 chunks per
+//      32 lanes needs the 8 rows on distinct chunk slots: chunk ^ wsw(row).
+template <int BN>
+__device__ __forceinline__ int wide_wsw(int r) {
+  if constexpr ((BN * 2) % 256 == 0)  // rows a multiple of 256 B: same bank base
+    return ((r & 3) << 1) | (r & 8);
+  else  // 384-B rows (BN = 192): odd rows start half-way round the banks
+    return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2);
+}
+
+// s_waitcnt vmcnt(N) then s_barrier, N a compile-time count.  Written as
+// inline assembly: the loads it waits for are issued from inline assembly,
+// which the compiler's own counter tracking does not see.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, bool FOLD>
+__global__ __launch_bounds__(64 * WGM * WGN, BM * BN <= 128 * 128 ? 2 : 1) void gemm_wide_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, uint16_t* __restrict__ y,
+    int M, int N, int K, int tm, int tn, int remap) {
+  constexpr int NW = WGM * WGN;
+  constexpr int TM = BM / WGM, TN = BN / WGN;  // wave tile
+  constexpr int SM = TM / 16, SN = TN / 16;    // 16 x 16 sub-tiles per wave
+  constexpr int XS = BM * 32;                  // x slab elements per stage
+  constexpr int WS = 32 * BN;                  // W slab elements per stage
+  constexpr int STAGE = XS + WS;
+  constexpr int XL = XS * 2 / 1024, WL = WS * 2 / 1024;  // 1 KB wave loads per stage
+  static_assert(XL % NW == 0 && WL % NW == 0, "loads must split evenly over the waves");
+  constexpr int XPW = XL / NW, WPW = WL / NW;  // x and W loads per wave per stage
+  constexpr int LPW = XPW + WPW;
+  constexpr int WCH = BN / 8;                  // 16-B chunks per W row
+  constexpr int SPS = 512 / 32;                // stages per segment (KC = 512)
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int tr_r = l16 >> 2, tr_c = lane & 3;
+
+  const int t = tile_of_block(blockIdx.x, tm, tn, remap);
+  const int m0 = (t % tm) * BM;
+  const int n0 = (t / tm) * BN;
+  const i32x4_t xr = make_rsrc_words(x, (uint32_t)((size_t)M * K * 2));
+  const i32x4_t wr = make_rsrc_words(W, (uint32_t)((size_t)K * N * 2));
+  const int nst = K / 32;
+
+  // this wave's loads: x regions wave * XPW + j (16 rows of 64 B each) and
+  // W regions wave * WPW + j (1 KB of the 32 x BN slab)
+  uint32_t goff[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    if (j < XPW) {
+      const int c = (wave * XPW + j) * 64 + lane, r = c >> 2, lc = (c & 3) ^ ((r >> 2) & 3);
+      goff[j] = ((uint32_t)(m0 + r) * (uint32_t)K + (uint32_t)(lc * 8)) * 2u;
+    } else {
+      const int c = (wave * WPW + j - XPW) * 64 + lane, r = c / WCH;
+      const int lc = (c % WCH) ^ wide_wsw<BN>(r);
+      goff[j] = ((uint32_t)r * (uint32_t)N + (uint32_t)(n0 + lc * 8)) * 2u;
+    }
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(BI_LDS void*)lds;
+  // loads of stage st into ring slot st % NS; the stage's advance along K
+  // is the scalar offset, and past the last stage it is 2^31, outside the
+  // buffer (zeros, no traffic), so that every stage issues exactly LPW
+  // loads per wave and the counter waits hold
+  auto dma = [&](int st) {
+    const bool valid = st < nst;
+    const uint32_t base = lds0 + (uint32_t)((st % NS) * STAGE * 2);
+    const uint32_t sx = valid ? (uint32_t)(st * 64) : 0x80000000u;
+    const uint32_t sw = valid ? (uint32_t)st * 32u * (uint32_t)N * 2u : 0x80000000u;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      if (j < XPW)
+        lds_dma16_so(xr, goff[j], sx, base + (uint32_t)((wave * XPW + j) * 1024));
+      else
+        lds_dma16_so(wr, goff[j], sw, base + (uint32_t)(XS * 2 + (wave * WPW + j - XPW) * 1024));
+    }
+  };
+
+  // fragment addresses (bytes in LDS) in the ring slot of the stage being
+  // read, advanced by one slot per stage
+  uint32_t xadr = lds0 + (uint32_t)(((wm * TM + l16) * 32 + ((g ^ ((l16 >> 2) & 3)) << 3)) * 2);
+  uint32_t wadr[SN][2];
+#pragma unroll
+  for (int tt = 0; tt < SN; ++tt) {
+    const int col = wn * TN + tt * 16 + 4 * tr_c;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * g + 4 * h + tr_r;
+      wadr[tt][h] = lds0 + (uint32_t)((XS + r * BN + (((col >> 3) ^ wide_wsw<BN>(r)) << 3) +
+                                       (col & 7)) * 2);
+    }
+  }
+  auto advance = [&](int st) {  // from the slot of stage st to that of st + 1
+    const uint32_t d = (st % NS == NS - 1) ? (uint32_t)(-(NS - 1) * STAGE * 2)
+                                           : (uint32_t)(STAGE * 2);
+    xadr += d;
+#pragma unroll
+    for (int tt = 0; tt < SN; ++tt) {
+      wadr[tt][0] += d;
+      wadr[tt][1] += d;
+    }
+  };
+  // One set of fragments, each reloaded with the next stage's as soon as
+  // the ops that read it have issued.
+  u32x4_t xf[SM], wf[SN];
+  auto read_w = [&](int tt) {
+    const u32x2_t b0 = lds_read_tr16_at(wadr[tt][0]);
+    const u32x2_t b1 = lds_read_tr16_at(wadr[tt][1]);
+    wf[tt] = u32x4_t{b0.x, b0.y, b1.x, b1.y};
+  };
+  auto read_x = [&](int sm) {
+    xf[sm] = *(const BI_LDS u32x4_t*)(uintptr_t)(xadr + (uint32_t)(sm * 16 * 32 * 2));
+  };
+
+  f32x4_t acc[SM][SN];
+  f32x4_t tot[FOLD ? SM : 1][FOLD ? SN : 1];
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < SN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // -0 + s == s exactly for every s, so the first fold copies the first
+  // segment's sum bit for bit
+#pragma unroll
+  for (int i = 0; i < (FOLD ? SM : 1); ++i)
+#pragma unroll
+    for (int j = 0; j < (FOLD ? SN : 1); ++j) tot[i][j] = f32x4_t{-0.f, -0.f, -0.f, -0.f};
+  // one 4-wide group at a time, so that only four accumulator values are
+  // copied out of the accumulator registers at once
+  auto fold = [&]() {
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j) {
+        tot[i][j] = tot[i][j] + acc[i][j];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+
+  // Stage st's K-block from the registers in two halves of the columns.
+  // The first half's W fragments are reloaded (stage st + 1) once it has
+  // issued, each x fragment once its row of the second half has, and the
+  // second half's W fragments at the end; the next stage needs them only
+  // after its first half.  A segment's first K-block starts from zero.
+  constexpr int SH = SN / 2;
+  auto stage = [&](int st, auto zero) {
+    constexpr bool Z = decltype(zero)::value;
+    // this wave's loads of stage st + 1 have landed (stages st + 2 ..
+    // st + NS - 2 may be in flight); after the barrier every wave's have,
+    // and every wave has consumed the fragments of stage st - 1, so that
+    // slot takes stage st + NS - 1
+    wait_vm_barrier<LPW * (NS - 3)>();
+    dma(st + NS - 1);
+    advance(st);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+      for (int tt = 0; tt < SH; ++tt)
+        acc[sm][tt] = mfma16x16x32(wf[tt], xf[sm], Z ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[sm][tt]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tt = 0; tt < SH; ++tt) read_w(tt);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sm = 0; sm < SM; ++sm) {
+#pragma unroll
+      for (int tt = SH; tt < SN; ++tt)
+        acc[sm][tt] = mfma16x16x32(wf[tt], xf[sm], Z ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[sm][tt]);
+      __builtin_amdgcn_sched_barrier(0);
+      read_x(sm);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int tt = SH; tt < SN; ++tt) read_w(tt);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // prologue: stages 0 .. NS - 2 in flight; stage 0's fragments read
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0) dma(s0);
+  wait_vm_barrier<LPW * (NS - 2)>();
+#pragma unroll
+  for (int tt = 0; tt < SN; ++tt) read_w(tt);
+#pragma unroll
+  for (int sm = 0; sm < SM; ++sm) read_x(sm);
+  // Segments of SPS stages (FOLD; else one run over all of K).
+  int st = 0;
+  for (;;) {
+    const int seg_end = FOLD ? min(nst, st + SPS) : nst;
+    stage(st, std::true_type{});
+    for (++st; st < seg_end; ++st) stage(st, std::false_type{});
+    if constexpr (FOLD) fold();
+    if (st >= nst) break;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+#pragma unroll
+  for (int sm = 0; sm < SM; ++sm) {
+    const int m = m0 + wm * TM + sm * 16 + l16;
+    if (m < M) {
+#pragma unroll
+      for (int tt = 0; tt < SN; ++tt) {
+        const int col = n0 + wn * TN + tt * 16 + g * 4;
+        if (n0 + wn * TN + tt * 16 < N) {  // N is a multiple of 16: sub-tiles all in or out
+          const f32x4_t v = FOLD ? tot[sm][tt] : acc[sm][tt];
+          *(u32x2_t*)&y[(size_t)m * N + col] =
+              u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      }
+    }
+  }
+}
+
+template __global__ void gemm_wide_kernel<128, 128, 2, 2, 5, true>(const uint16_t*,
+                                                                   const uint16_t*, uint16_t*, int,
+                                                                   int, int, int, int, int);
+template __global__ void gemm_wide_kernel<256, 256, 2, 4, 4, false>(const uint16_t*,
+                                                                    const uint16_t*, uint16_t*, int,
+                                                                    int, int, int, int, int);
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 static constexpr int BI_KC = 512;  // invariant segment length
@@ -517,15 +774,20 @@ static constexpr int SKINNY_MAX_M = 64;
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Which kernels run for (M, N, K).  The bits never depend on it.
-static constexpr int TILE_MIN_TILES = 192;  // fewer tiles than this: split K into slices
+// Which kernels run for (M, N, K).  The bits of bi_gemm never depend on it.
+static constexpr int TILE_MIN_TILES = 192;  // fewer tiles than this leave CUs idle
 
-enum class GemmPath { Tile, TileSlice, Skinny };
-static GemmPath gemm_path(int64_t M, int64_t N) {
-  if (M > SKINNY_MAX_M)
-    return ceil_div(M, TILE_BM) * ceil_div(N, TL_BN) >= TILE_MIN_TILES ? GemmPath::Tile
-                                                                         : GemmPath::TileSlice;
-  return GemmPath::Skinny;
+// Invariant schedule, M > 64: 256 x 128 tiles with every segment in registers
+// when there are enough of them; else 128 x 128 tiles with every segment in
+// registers when those fill the chip (o and down at M = 1024: 256 tiles
+// instead of 128, and no segment sums through memory); else the K-slice
+// path.  The fast twin has no 128 x 128 path (it slices K freely instead).
+enum class GemmPath { Tile, Fold128, TileSlice, Skinny };
+static GemmPath gemm_path(int64_t M, int64_t N, bool fast) {
+  if (M <= SKINNY_MAX_M) return GemmPath::Skinny;
+  if (ceil_div(M, TILE_BM) * ceil_div(N, TL_BN) >= TILE_MIN_TILES) return GemmPath::Tile;
+  if (!fast && ceil_div(M, 128) * ceil_div(N, 128) >= TILE_MIN_TILES) return GemmPath::Fold128;
+  return GemmPath::TileSlice;
 }
 
 // K slice of the tile kernel: the invariant schedule always uses 512 (one
@@ -564,8 +826,8 @@ static int64_t slice_kc(int64_t M, int64_t N, int64_t K, bool fast, int num_cus)
 }
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool fast, int num_cus) {
-  const GemmPath p = gemm_path(M, N);
-  if (p == GemmPath::Tile) return 0;
+  const GemmPath p = gemm_path(M, N, fast);
+  if (p == GemmPath::Tile || p == GemmPath::Fold128) return 0;
   const int64_t kc = p == GemmPath::TileSlice ? slice_kc(M, N, K, fast, num_cus) : BI_KC;
   return (size_t)ceil_div(K, kc) * (size_t)M * (size_t)N * sizeof(float);
 }
@@ -595,13 +857,25 @@ static int launch_skinny(const uint16_t* x, const uint16_t* W, float* part, int6
 int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, int64_t N,
                 int64_t K, void* ws, size_t ws_bytes, hipStream_t stream, bool fast, int num_cus) {
   const int64_t S = ceil_div(K, BI_KC);
-  const GemmPath p = gemm_path(M, N);
+  const GemmPath p = gemm_path(M, N, fast);
+  if (p == GemmPath::Fold128) {
+    const int64_t tm = ceil_div(M, 128), tn = ceil_div(N, 128);
+    hipLaunchKernelGGL((gemm_wide_kernel<128, 128, 2, 2, 5, true>), dim3((unsigned)(tm * tn)),
+                       dim3(256), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)tm, (int)tn,
+                       tile_remap(tm, tn));
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+  }
   if (p == GemmPath::Tile || p == GemmPath::TileSlice) {
     const int64_t tm = ceil_div(M, TILE_BM), tn = ceil_div(N, TL_BN);
     const int remap = tile_remap(tm, tn);
     if (p == GemmPath::Tile) {
       dim3 grid((unsigned)(tm * tn));
-      if (fast)
+      const int64_t tn2 = ceil_div(N, 256);
+      if (fast && tm * tn2 >= TILE_MIN_TILES)  // 256 x 256 tiles still fill the chip
+        hipLaunchKernelGGL((gemm_wide_kernel<256, 256, 2, 4, 4, false>), dim3((unsigned)(tm * tn2)),
+                           dim3(512), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)tm,
+                           (int)tn2, tile_remap(tm, tn2));
+      else if (fast)
         hipLaunchKernelGGL((gemm_tile_kernel<false, false>), grid, dim3(512), 0, stream, x, W, y,
                            (int)M, (int)N, (int)K, (int)K, (int)tm, (int)tn, remap, (float*)nullptr,
                            1);

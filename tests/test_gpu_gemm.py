@@ -186,6 +186,26 @@ def test_slice_path_runs_of_segments(gpu, M, N, K):
     check_close_bf16(bits(y[rows]), oracle.gemm(bits(x[rows]), bits(w)), what=f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1000, 4096, 14336), (1025, 4032, 4640), (520, 6144, 1056),
+                                   (777, 4160, 4096)])
+def test_fold128_path_ragged_shapes(gpu, M, N, K):
+    """The 128 x 128 register-fold path (256 x 128 tiles too few, 128 x 128
+    tiles enough to fill the chip): a last tile row of 104, 1, 8 and 9 rows,
+    a last tile column of 64 columns (N % 128 == 64), K ending in a short
+    segment of one K-block (K % 512 == 32).  Every row of the first 64 matches the
+    skinny path bit for bit (one call at M = 64), sampled rows match
+    single-row calls, and the oracle within tolerance."""
+    x, w = synth.gemm_inputs(M, K, N, seed=M * 3 + K, device=DEV)
+    assert gpu.gemm_workspace_bytes(M, N, K) == 0      # every segment stays in registers
+    y = gpu.gemm(x, w)
+    assert same_bits(gpu.gemm(x[:64].contiguous(), w), y[:64])
+    rows = [0, 127, 128, M // 2, M - 1]
+    for r in rows:
+        assert same_bits(gpu.gemm(x[r:r + 1].contiguous(), w), y[r:r + 1]), f"row {r}"
+    torch.cuda.synchronize()
+    check_close_bf16(bits(y[rows]), oracle.gemm(bits(x[rows]), bits(w)), what=f"{M}x{N}x{K}")
+
+
 def test_run_to_run_and_row_permutation(gpu):
     x, w = synth.gemm_inputs(300, 4096, 4096, seed=4, device=DEV)
     base = gpu.gemm(x, w)
@@ -199,9 +219,14 @@ def test_run_to_run_and_row_permutation(gpu):
         assert same_bits(gpu.gemm(x[:7].contiguous(), w), small)
 
 
-@pytest.mark.parametrize("M", [1, 16, 64, 2048])
-def test_fast_twin_parity(gpu, M):
-    K, N = 4096, 4096
+@pytest.mark.parametrize("M,N", [(1, 4096), (16, 4096), (64, 4096), (300, 4096), (2048, 4096),
+                                 (2048, 6208), (600, 28672), (1025, 6144)])
+def test_fast_twin_parity(gpu, M, N):
+    """The fast twin on each of its paths (skinny; K-slice at M = 300;
+    256 x 128 tiles; 256 x 256 tiles, with a last tile column of 64 columns
+    at N = 6208 and a last tile row of 88 rows at M = 600), within tolerance
+    of the oracle."""
+    K = 4096
     x, w = synth.gemm_inputs(M, K, N, seed=5, device=DEV)
     y = gpu.gemm_fast(x, w)
     torch.cuda.synchronize()
