@@ -213,8 +213,10 @@ __global__ __launch_bounds__(512, 4) void gemm_skinny_kernel(
 }
 
 // Ordered fold of segment sums: y = bf16(((p0 + p1) + p2) + ...), fp32.
-// One lane per (row, 4 columns); every segment's load is issued before the
-// adds.  grid = (ceil(N/256), M), block = 64.
+// One lane per (row, 4 columns).  The loads of up to 32 segments are issued
+// together, before any add (one memory round trip for K <= 16384), then
+// added in index order.  grid = (ceil(N/256), M), block = 64.
+static constexpr int FOLD_BATCH = 32;
 __global__ __launch_bounds__(64) void gemm_fold_kernel(const float* __restrict__ part,
                                                        uint16_t* __restrict__ y, int M, int N,
                                                        int S) {
@@ -223,14 +225,16 @@ __global__ __launch_bounds__(64) void gemm_fold_kernel(const float* __restrict__
   if (c4 * 4 >= N) return;
   const f32x4_t* p = (const f32x4_t*)(part + (size_t)m * N) + c4;
   const size_t step = (size_t)M * N / 4;
-  f32x4_t acc = p[0];
-  for (int s0 = 1; s0 < S; s0 += 8) {
-    f32x4_t v[8];
+  f32x4_t acc;
+  for (int s0 = 0; s0 < S; s0 += FOLD_BATCH) {
+    f32x4_t v[FOLD_BATCH];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < FOLD_BATCH; ++u)
       if (s0 + u < S) v[u] = p[(size_t)(s0 + u) * step];
+    // segment 0 is taken as it is (the fold starts from the first sum)
+    acc = s0 == 0 ? v[0] : acc + v[0];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 1; u < FOLD_BATCH; ++u)
       if (s0 + u < S) acc = acc + v[u];
   }
   uint32_t* out = (uint32_t*)(y + (size_t)m * N + c4 * 4);
