@@ -50,8 +50,10 @@ def on_stream(stream, fn, *args):
     return out
 
 
-@pytest.mark.parametrize("M", [1, 16, 40, 300, 2048])
+@pytest.mark.parametrize("M", [1, 16, 40, 300, 1024, 2048])
 def test_gemm_bits_under_cu_masks(gpu, masked_streams, M):
+    """Every bi_gemm path: skinny (1, 16, 40), K-slice (300), 128 x 128
+    register fold (1024) and 256 x 128 tiles (2048)."""
     x, w = synth.gemm_inputs(M, 4096, 4096, seed=31 + M, device=DEV)
     ref = gpu.gemm(x, w)
     torch.cuda.synchronize()
@@ -106,11 +108,13 @@ def test_bits_under_concurrent_memory_load(gpu):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 4096, 6144), (2048, 4096, 6144), (256, 14336, 4096)])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 6144), (2048, 4096, 6144), (256, 14336, 4096),
+                                   (1024, 14336, 4096)])
 def test_gemm_hundred_repeats(gpu, M, K, N):
-    """Bitwise stable over 100 calls: the skinny path, the tile path, and the
+    """Bitwise stable over 100 calls: the skinny path, the tile path, the
     K-slice path with runs of four segments per workgroup (down at M = 256),
-    whose segment-sum stores go out while the load ring keeps running."""
+    whose segment-sum stores go out while the load ring keeps running, and
+    the 128 x 128 register-fold path (down at M = 1024)."""
     x, w = synth.gemm_inputs(M, K, N, seed=36, device=DEV)
     ref = gpu.gemm(x, w)
     outs = [gpu.gemm(x, w) for _ in range(100)]
