@@ -142,3 +142,24 @@ def test_default_scale_through_the_c_abi(gpu):
         np.testing.assert_array_equal(o, outs[0])
     want = oracle.paged_decode_attn(synth.to_bits(q), synth.to_bits(kv), bt, cl, HKV, PS)
     check_close_bf16(outs[0], want, what="default scale")
+
+
+def test_longest_supported_context(gpu):
+    """A request at the largest context the entry point takes (262144
+    tokens: 1024 chunks, a 1 GiB page pool): within tolerance of the oracle,
+    and bitwise the same alone as beside a one-token request with a
+    max_ctx_len that sizes the grid for both."""
+    L = 262144
+    ctx = np.array([L, 1], np.int32)
+    q, kv, bt, cl = synth.attn_inputs(ctx, seed=91)
+    qb, kvb = synth.to_bits(q), synth.to_bits(kv)
+    kvd = kv.to(DEV)
+    both = run(gpu, q.to(DEV), kvd, bt, cl, max_ctx=L)
+    alone = run(gpu, q[:1].contiguous().to(DEV), kvd, bt[:1], cl[:1], max_ctx=L)
+    np.testing.assert_array_equal(alone, both[:1])
+    want = oracle.paged_decode_attn(qb[:1], kvb, bt[:1], cl[:1], HKV, PS)
+    check_close_bf16(alone, want, what="262144-token context")
+    # the one-token request reads its single value vector exactly
+    page, slot = int(bt[1, 0]), 0
+    for h in range(32):
+        np.testing.assert_array_equal(both[1, h], kvb[page, 1, h // 4, slot])
