@@ -565,7 +565,7 @@ __device__ __forceinline__ void wait_vm_barrier() {
 template <int BM, int BN, int WGM, int WGN, int NS, bool FOLD>
 __global__ __launch_bounds__(64 * WGM * WGN, BM * BN <= 128 * 128 ? 2 : 1) void gemm_wide_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, uint16_t* __restrict__ y,
-    int M, int N, int K, int tm, int tn, int remap) {
+    int M, int N, int K, int tm, int tn, int remap, int n_base) {
   constexpr int NW = WGM * WGN;
   constexpr int TM = BM / WGM, TN = BN / WGN;  // wave tile
   constexpr int SM = TM / 16, SN = TN / 16;    // 16 x 16 sub-tiles per wave
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, BM * BN <= 128 * 128 ? 2 : 1) void 
 
   const int t = tile_of_block(blockIdx.x, tm, tn, remap);
   const int m0 = (t % tm) * BM;
-  const int n0 = (t / tm) * BN;
+  const int n0 = n_base + (t / tm) * BN;  // tiles of columns [n_base, N)
   const i32x4_t xr = make_rsrc_words(x, (uint32_t)((size_t)M * K * 2));
   const i32x4_t wr = make_rsrc_words(W, (uint32_t)((size_t)K * N * 2));
   const int nst = K / 32;
@@ -764,10 +764,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, BM * BN <= 128 * 128 ? 2 : 1) void 
 
 template __global__ void gemm_wide_kernel<128, 128, 2, 2, 5, true>(const uint16_t*,
                                                                    const uint16_t*, uint16_t*, int,
-                                                                   int, int, int, int, int);
+                                                                   int, int, int, int, int, int);
 template __global__ void gemm_wide_kernel<256, 256, 2, 4, 4, false>(const uint16_t*,
                                                                     const uint16_t*, uint16_t*, int,
-                                                                    int, int, int, int, int);
+                                                                    int, int, int, int, int, int);
 
 // ---------------------------------------------------------------------------
 // Host side
@@ -841,6 +841,35 @@ static int tile_remap(int64_t tm, int64_t tn) {
   return (tm % 8 == 0 && tn % 4 == 0) ? 3 : (tn % 8 == 0) ? 2 : ((tm * tn) % 8 == 0) ? 1 : 0;
 }
 
+// The invariant schedule on 256 x 128 tiles.  When they take more than one
+// round of the CUs and the last round is partial, the tile columns of that
+// round are computed as 128 x 128 tiles instead (twice as many, each half the
+// work, one per CU in a second launch): e.g. qkv at M = 2048, 384 tiles, runs
+// 256 of 256 x 128 and then 256 of 128 x 128 where it ran two rounds of
+// 256 x 128.  Both kernels compute every output with the same schedule, so
+// which one computes a column changes no bits.
+static int launch_tile_invariant(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M,
+                                 int64_t N, int64_t K, int64_t tm, int64_t tn, hipStream_t stream) {
+  const int64_t C = 256;  // rounds of a 256-CU chip (a constant: the plan reads no device state)
+  const int64_t T = tm * tn;
+  int64_t k = 0;  // tile columns moved to the 128 x 128 launch
+  if (T > C && T % C != 0) {
+    k = ceil_div(T % C, tm);
+    if (k >= tn || ceil_div(M, 128) * k > C) k = 0;  // the 128 x 128 tiles must fit one round
+  }
+  const int64_t tn1 = tn - k;
+  hipLaunchKernelGGL((gemm_tile_kernel<true, false>), dim3((unsigned)(tm * tn1)), dim3(512), 0,
+                     stream, x, W, y, (int)M, (int)N, (int)K, BI_KC, (int)tm, (int)tn1,
+                     tile_remap(tm, tn1), (float*)nullptr, 1);
+  if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
+  if (k == 0) return BI_OK;
+  const int64_t tm2 = ceil_div(M, 128), tn2 = ceil_div(N - tn1 * TL_BN, 128);
+  hipLaunchKernelGGL((gemm_wide_kernel<128, 128, 2, 2, 5, true>), dim3((unsigned)(tm2 * tn2)),
+                     dim3(256), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)tm2, (int)tn2,
+                     tile_remap(tm2, tn2), (int)(tn1 * TL_BN));
+  return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
 // The skinny kernel for M <= 64, x padded to 16, 32 or 64 rows: the S
 // segment sums of every 128-column tile into part [S][M][N].
 static int launch_skinny(const uint16_t* x, const uint16_t* W, float* part, int64_t M, int64_t N,
@@ -866,7 +895,7 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
     const int64_t tm = ceil_div(M, 128), tn = ceil_div(N, 128);
     hipLaunchKernelGGL((gemm_wide_kernel<128, 128, 2, 2, 5, true>), dim3((unsigned)(tm * tn)),
                        dim3(256), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)tm, (int)tn,
-                       tile_remap(tm, tn));
+                       tile_remap(tm, tn), 0);
     return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
   }
   if (p == GemmPath::Tile || p == GemmPath::TileSlice) {
@@ -878,15 +907,13 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
       if (fast && tm * tn2 >= TILE_MIN_TILES)  // 256 x 256 tiles still fill the chip
         hipLaunchKernelGGL((gemm_wide_kernel<256, 256, 2, 4, 4, false>), dim3((unsigned)(tm * tn2)),
                            dim3(512), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)tm,
-                           (int)tn2, tile_remap(tm, tn2));
+                           (int)tn2, tile_remap(tm, tn2), 0);
       else if (fast)
         hipLaunchKernelGGL((gemm_tile_kernel<false, false>), grid, dim3(512), 0, stream, x, W, y,
                            (int)M, (int)N, (int)K, (int)K, (int)tm, (int)tn, remap, (float*)nullptr,
                            1);
       else
-        hipLaunchKernelGGL((gemm_tile_kernel<true, false>), grid, dim3(512), 0, stream, x, W, y,
-                           (int)M, (int)N, (int)K, BI_KC, (int)tm, (int)tn, remap, (float*)nullptr,
-                           1);
+        return launch_tile_invariant(x, W, y, M, N, K, tm, tn, stream);
       return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
     }
     const int64_t kc = slice_kc(M, N, K, fast, num_cus);
