@@ -310,6 +310,23 @@ def run_extras(torch, bi, synth, dev, args, M, acts, wsets):
     # their own graphs and replayed alternately (medians of five rounds)
     per = {}
     wcopies = make_linear_copies(torch, synth, dev)
+    # what HBM delivers with nothing else to do: a streaming read of the same
+    # weight copies, back to back in one graph (the decode steps' bound)
+    from invariant_bi_gemm_02_amd import ceiling_read, CEILING_READ_OUT_WORDS
+    rout = torch.empty(CEILING_READ_OUT_WORDS, dtype=torch.int32, device=dev)
+    read_us = {}
+    for name, K, N in LINEARS:
+        cp = wcopies[name]
+        calls = [(cp[i % len(cp)], rout) for i in range(max(20, 2 * len(cp)))]
+        read_us[name] = graph_time_us(torch, lambda buf, out: ceiling_read(buf, out=out), calls)
+    extras["read_weights"] = {
+        name: {"bytes": K * N * 2, "us": read_us[name],
+               "gbs": K * N * 2 / (read_us[name] * 1e-6) / 1e9,
+               "frac_of_8tbs": K * N * 2 / (read_us[name] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        for name, K, N in LINEARS}
+    extras["read_weights"]["what"] = (
+        "bi_ceiling_read: every 16-B chunk of the weight loaded once, 1 KB per wave "
+        "instruction, over the same >= 512 MB of rotated copies as the sweep")
     for Mx in sorted(set([M, args.decode_m, 1, 64, 128, 256, 512, 1024])):
         ax = make_acts(torch, synth, Mx, dev, seed=1) if Mx != M else acts
         ox = {name: torch.empty((Mx, N), dtype=torch.bfloat16, device=dev)
@@ -335,6 +352,9 @@ def run_extras(torch, bi, synth, dev, args, M, acts, wsets):
                          "weight_copies": len(wcopies[name])}
             lin[name]["hbm_frac"] = lin[name]["gbs"] / HBM_PEAK_GBS
             lin[name]["mfma_frac"] = lin[name]["tflops"] / MFMA_BF16_PEAK_TFS
+            if same:  # streaming W is the bound: set beside a plain read of W
+                lin[name]["read_ceiling_us"] = read_us[name]
+                lin[name]["frac_of_read_ceiling"] = read_us[name] / tb
         tot_b = sum(row["bi"].values())
         tot_f = sum(row["fast"].values())
         byt = sum(gemm_bytes(Mx, K, N) for _, K, N in LINEARS)
@@ -346,6 +366,9 @@ def run_extras(torch, bi, synth, dev, args, M, acts, wsets):
                         "hbm_frac": byt / (tot_b * 1e-6) / 1e9 / HBM_PEAK_GBS,
                         "tflops": fl / (tot_b * 1e-6) / 1e12,
                         "mfma_frac": fl / (tot_b * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS}
+        if same:
+            per[str(Mx)]["read_ceiling_us"] = sum(read_us.values())
+            per[str(Mx)]["frac_of_read_ceiling"] = sum(read_us.values()) / tot_b
     del wcopies
     torch.cuda.empty_cache()
     extras["by_M"] = per

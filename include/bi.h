@@ -427,6 +427,20 @@ int bi_add(const bi_bf16 *a, const bi_bf16 *b, bi_bf16 *out, int64_t n,
 int bi_ceiling_mfma(float *out, int64_t iters, int64_t workgroups,
                     void *stream);
 
+/* Measurement helper (no operation's path uses it): a streaming read of one
+ * device buffer, so that a benchmark can set a bandwidth-bound kernel beside
+ * the time the same bytes take to arrive with nothing else to do.  Every
+ * 16-byte chunk of p[0 .. bytes) is loaded once (consecutive lanes on
+ * consecutive chunks), the words are XOR-ed together per wave, and wave w of
+ * workgroup b writes out[4 b + w].  At most BI_CEILING_READ_OUT_WORDS / 4
+ * workgroups run, so out must hold BI_CEILING_READ_OUT_WORDS words (device
+ * memory, 4-byte aligned); words past the launch's workgroups are not
+ * written.  p is read only.  Requirements: 1 <= bytes <= 2^40, bytes % 16
+ * == 0, p 16-byte aligned.  Status: BI_ERR_NULL for a null p or out,
+ * BI_ERR_SHAPE for a size out of range, BI_ERR_UNSUPPORTED for alignment. */
+#define BI_CEILING_READ_OUT_WORDS 8192
+int bi_ceiling_read(const void *p, int64_t bytes, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     gemm_fast,
     gemm_noalloc,
     ceiling_mfma,
+    ceiling_read,
+    CEILING_READ_OUT_WORDS,
     gemm_workspace_bytes,
     gemm_fast_workspace_bytes,
     rmsnorm,

@@ -40,7 +40,7 @@ EXPORTS = ("bi_version", "bi_status_string", "bi_gemm_workspace_bytes", "bi_gemm
            "bi_silu_mul", "bi_add", "bi_paged_prefill_attn",
            "bi_gemm_segments", "bi_gemm_fold", "bi_sample", "bi_verify_commit",
            "bi_sample_workspace_bytes", "bi_add_rmsnorm", "bi_gemm_noalloc",
-           "bi_ceiling_mfma")
+           "bi_ceiling_mfma", "bi_ceiling_read")
 
 _lock = threading.Lock()
 _lib = None
@@ -97,6 +97,7 @@ def load(path: str | None = None):
             "bi_gemm_fold": [vp, vp, i64, i64, i64, vp],
             "bi_gemm_noalloc": [vp, vp, vp, i64, i64, i64, vp],
             "bi_ceiling_mfma": [vp, i64, i64, vp],
+            "bi_ceiling_read": [vp, i64, vp, vp],
         }
         for f, a in sigs.items():
             getattr(lib, f).restype = ctypes.c_int
@@ -206,6 +207,25 @@ def ceiling_mfma(iters: int, workgroups: int, out=None, device=None):
     _raise(lib.bi_ceiling_mfma(out.data_ptr(), int(iters), int(workgroups), _stream(dev)),
            "bi_ceiling_mfma")
     return out, float(workgroups) * 4 * iters * 8 * 16384
+
+
+CEILING_READ_OUT_WORDS = 8192
+
+
+def ceiling_read(buf: torch.Tensor, out=None):
+    """Stream every byte of the device tensor `buf` once (a measurement
+    helper); returns the per-wave output words (int32 tensor of
+    CEILING_READ_OUT_WORDS, allocated here when None)."""
+    lib = load()
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous device tensor")
+    if out is None:
+        out = torch.empty(CEILING_READ_OUT_WORDS, dtype=torch.int32, device=buf.device)
+    elif out.numel() < CEILING_READ_OUT_WORDS or out.element_size() != 4 or not out.is_cuda:
+        raise ValueError("out must be a device tensor of CEILING_READ_OUT_WORDS 4-byte words")
+    _raise(lib.bi_ceiling_read(buf.data_ptr(), buf.numel() * buf.element_size(), out.data_ptr(),
+                               _stream(buf.device)), "bi_ceiling_read")
+    return out
 
 
 def gemm_noalloc(x, w, out=None):

@@ -1,6 +1,10 @@
-// bi_ceiling.hip -- a matrix-core-only loop, so that measurements can quote
-// the bf16 rate the chip sustains at the clock it holds under matrix-core
-// load beside the published peak.  Not part of any operation's path.
+// bi_ceiling.hip -- measurement helpers, not part of any operation's path:
+//   a matrix-core-only loop, so that measurements can quote the bf16 rate the
+//   chip sustains at the clock it holds under matrix-core load beside the
+//   published peak;
+//   a streaming read of one buffer, so that a bandwidth-bound kernel can be
+//   set beside the time HBM takes to deliver the same bytes with nothing
+//   else to do.
 //
 // Each wave runs `iters` rounds of eight independent chains of
 // v_mfma_f32_16x16x32_bf16 (the instruction every GEMM path issues) on
@@ -59,7 +63,48 @@ int launch_mfma_ceiling(float* out, int64_t iters, int64_t workgroups, hipStream
   return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
 
+// Streaming read: every 16-byte chunk of p[0 .. n16) is loaded once, four
+// chunks per lane per round (consecutive lanes on consecutive chunks, 1 KB per
+// wave instruction), and XOR-ed into a register; each wave writes one word,
+// out[4 * blockIdx.x + wave], so that no load is optimised away.
+static constexpr int READ_UNROLL = 4;
+__global__ __launch_bounds__(256) void read_ceiling_kernel(const u32x4_t* __restrict__ p,
+                                                           int64_t n16, uint32_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * READ_UNROLL;
+  uint32_t acc = 0;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * READ_UNROLL + threadIdx.x; base < n16;
+       base += stride) {
+    u32x4_t v[READ_UNROLL];
+#pragma unroll
+    for (int u = 0; u < READ_UNROLL; ++u) {
+      const int64_t i = base + (int64_t)u * 256;
+      v[u] = i < n16 ? p[i] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < READ_UNROLL; ++u) acc ^= (v[u][0] ^ v[u][1]) ^ (v[u][2] ^ v[u][3]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+  if ((threadIdx.x & 63) == 0) out[(size_t)blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
+}
+
+int launch_read_ceiling(const void* p, int64_t bytes, uint32_t* out, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  const int64_t per_wg = 256 * READ_UNROLL;
+  const int64_t grid = std::min<int64_t>((n16 + per_wg - 1) / per_wg, BI_CEILING_READ_OUT_WORDS / 4);
+  hipLaunchKernelGGL(read_ceiling_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const u32x4_t*)p, n16, out);
+  return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
 }  // namespace bi
+
+extern "C" int bi_ceiling_read(const void* p, int64_t bytes, uint32_t* out, void* stream) {
+  if (!p || !out) return BI_ERR_NULL;
+  if (bytes <= 0 || bytes > ((int64_t)1 << 40)) return BI_ERR_SHAPE;
+  if (bytes % 16 != 0 || ((uintptr_t)p & 15u) || ((uintptr_t)out & 3u)) return BI_ERR_UNSUPPORTED;
+  return bi::launch_read_ceiling(p, bytes, out, (hipStream_t)stream);
+}
 
 extern "C" int bi_ceiling_mfma(float* out, int64_t iters, int64_t workgroups, void* stream) {
   if (!out) return BI_ERR_NULL;

@@ -64,6 +64,7 @@ int launch_add(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t n,
 
 // Matrix-core-only loop for measured ceilings (bi_ceiling.hip)
 int launch_mfma_ceiling(float* out, int64_t iters, int64_t workgroups, hipStream_t stream);
+int launch_read_ceiling(const void* p, int64_t bytes, uint32_t* out, hipStream_t stream);
 
 // Schedule constants reported by bi_version().
 static constexpr int SCHED_GEMM_KB = 32;

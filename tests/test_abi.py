@@ -62,6 +62,19 @@ def P(v):
     return ctypes.c_void_p(v)
 
 
+def test_ceiling_read_argument_checks(lib):
+    """The streaming-read helper refuses bad arguments before touching a
+    device."""
+    ok = 0x1000
+    assert lib.bi_ceiling_read(None, 16, P(ok), None) == -1
+    assert lib.bi_ceiling_read(P(ok), 16, None, None) == -1
+    assert lib.bi_ceiling_read(P(ok), 0, P(ok), None) == -2
+    assert lib.bi_ceiling_read(P(ok), (1 << 40) + 16, P(ok), None) == -2
+    assert lib.bi_ceiling_read(P(ok), 24, P(ok), None) == -3
+    assert lib.bi_ceiling_read(P(ok + 8), 16, P(ok), None) == -3
+    assert lib.bi_ceiling_read(P(ok), 16, P(ok + 2), None) == -3
+
+
 def test_gemm_argument_checks(lib):
     ok = 0x1000
     assert lib.bi_gemm(None, P(ok), P(ok), 1, 64, 32, None, 0, None) == -1
