@@ -933,8 +933,11 @@ def bench_attn(torch, bi, synth, dev, args):
     lengths uniform in [512, 32768]).  Small batches rotate over copies of
     their page pool totalling >= 512 MB so that the 256 MB last-level cache
     cannot serve the K/V; calls are replayed from a graph of back-to-back
-    calls (bi and fast alternately, medians)."""
+    calls (bi and fast alternately, medians).  Beside each, a streaming read
+    of the same pools (bi_ceiling_read) gives the rate those bytes arrive at
+    with nothing else to do."""
     import numpy as np
+    from invariant_bi_gemm_02_amd import ceiling_read, CEILING_READ_OUT_WORDS
     out = {}
     for B in (1, 8, 64):
         ctx = synth.ctx_lens_uniform(B, seed=3 + B)
@@ -952,10 +955,19 @@ def bench_attn(torch, bi, synth, dev, args):
         ff = lambda q, kv, bt, cl, out: bi.paged_decode_attn_fast(q, kv, bt, cl, max_ctx_len=mc,
                                                                   out=out)
         tb, tf = paired_graph_time_us(torch, fb, ff, calls)
+        # a streaming read of the same page pools, back to back: the rate HBM
+        # gives these bytes read contiguously with nothing else to do
+        rout = torch.empty(CEILING_READ_OUT_WORDS, dtype=torch.int32, device=dev)
+        pool_bytes = sets[0][1].numel() * 2
+        rcalls = [(sets[i % copies][1], rout) for i in range(reps)]
+        tr = graph_time_us(torch, lambda buf, out: ceiling_read(buf, out=out), rcalls)
+        read_gbs = pool_bytes / (tr * 1e-6) / 1e9
         out[str(B)] = {"B": B, "mean_ctx": float(np.mean(ctx)), "kv_copies": copies,
                        "us": tb, "fast_us": tf, "overhead_pct": (tb / tf - 1) * 100,
                        "gbs": per_call / (tb * 1e-6) / 1e9,
-                       "hbm_frac": per_call / (tb * 1e-6) / 1e9 / HBM_PEAK_GBS}
+                       "hbm_frac": per_call / (tb * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                       "read_pool_us": tr, "read_pool_gbs": read_gbs,
+                       "frac_of_read_ceiling": per_call / (tb * 1e-6) / 1e9 / read_gbs}
         del sets, calls, o
         torch.cuda.empty_cache()
     return out
