@@ -163,3 +163,25 @@ def test_longest_supported_context(gpu):
     page, slot = int(bt[1, 0]), 0
     for h in range(32):
         np.testing.assert_array_equal(both[1, h], kvb[page, 1, h // 4, slot])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_groups_and_lengths_vs_oracle_and_alone(gpu, seed):
+    """Seeded random cases over the group sizes the kernel has (G = 1, 2, 4,
+    8 query heads per kv head), batch sizes 1-6 and context lengths 1-3000
+    (tile and chunk boundaries included at random): within tolerance of the
+    oracle, and every request alone bitwise equal to its row in the batch."""
+    rng = np.random.default_rng(500 + seed)
+    G = [1, 2, 4, 8, 2, 8][seed]
+    hkv = [8, 4, 2, 1, 2, 4][seed]
+    B = int(rng.integers(1, 7))
+    ctx = rng.integers(1, 3001, size=B).astype(np.int32)
+    ctx[rng.integers(0, B)] = [1, 64, 256, 257, 512, 2048][seed]
+    q, kv, bt, cl = synth.attn_inputs(ctx, seed=600 + seed, Hq=G * hkv, Hkv=hkv)
+    qb, kvb = synth.to_bits(q), synth.to_bits(kv)
+    got = run(gpu, qb, kvb, bt, cl)
+    want = oracle.paged_decode_attn(qb, kvb, bt, cl, hkv, PS)
+    check_close_bf16(got, want, what=f"G={G} Hkv={hkv} ctx={ctx.tolist()}")
+    for b in range(B):
+        alone = run(gpu, qb[b:b + 1], kvb, bt[b:b + 1], cl[b:b + 1])
+        np.testing.assert_array_equal(alone[0], got[b])

@@ -226,6 +226,25 @@ def test_partial_round_retiled(gpu, M, N, K):
     check_close_bf16(bits(y[rows]), oracle.gemm(bits(x[rows]), bits(w)), what=f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_vs_oracle_and_single_rows(gpu, seed):
+    """Seeded random shapes (M 1-299, N a multiple of 64 up to 1024, K a
+    multiple of 32 up to 2048, so every path below M = 300 and ragged last
+    segments come up): within tolerance of the oracle, and sampled rows
+    computed alone bitwise equal to their rows in the batch."""
+    rng = np.random.default_rng(300 + seed)
+    M = int(rng.integers(1, 300))
+    N = 64 * int(rng.integers(1, 17))
+    K = 32 * int(rng.integers(1, 65))
+    x, w = synth.gemm_inputs(M, K, N, seed=700 + seed, w_std=0.5)
+    xd, wd = x.to(DEV), w.to(DEV)
+    y = gpu.gemm(xd, wd)
+    torch.cuda.synchronize()
+    check_close_bf16(bits(y), oracle.gemm(bits(x), bits(w)), what=f"{M}x{N}x{K}")
+    for r in sorted({0, M - 1, int(rng.integers(0, M))}):
+        assert same_bits(gpu.gemm(xd[r:r + 1].contiguous(), wd), y[r:r + 1]), f"row {r}"
+
+
 def test_run_to_run_and_row_permutation(gpu):
     x, w = synth.gemm_inputs(300, 4096, 4096, seed=4, device=DEV)
     base = gpu.gemm(x, w)
