@@ -528,6 +528,9 @@ __global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
 //     invariant schedule where 256 x 128 tiles would leave CUs idle but
 //     128 x 128 tiles fill the chip (e.g. o and down at M = 1024), so every
 //     segment stays in registers instead of going through the workspace;
+//   256 x 192, FOLD (8 waves of 64 x 96, one workgroup per CU, 251
+//     registers): the invariant schedule where 256 x 128 tiles would leave a
+//     partial round and 256 x 192 tiles make whole ones (qkv at M = 2048);
 //   256 x 256, one chain over all of K (8 waves of 64 x 128): the fast
 //     twin's large-M tile, half the L2 bytes per flop of 256 x 128.  The
 //     invariant schedule cannot use it: the fold's running total doubles the
@@ -573,9 +576,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, BM * BN <= 128 * 128 ? 2 : 1) void 
   constexpr int WS = 32 * BN;                  // W slab elements per stage
   constexpr int STAGE = XS + WS;
   constexpr int XL = XS * 2 / 1024, WL = WS * 2 / 1024;  // 1 KB wave loads per stage
-  static_assert(XL % NW == 0 && WL % NW == 0, "loads must split evenly over the waves");
-  constexpr int XPW = XL / NW, WPW = WL / NW;  // x and W loads per wave per stage
-  constexpr int LPW = XPW + WPW;
+  // Either every wave loads XL / NW of the x slab and WL / NW of the W slab
+  // (EVEN), or, where those do not divide, the first NW / 2 waves load the x
+  // slab and the others the W slab (e.g. 256 x 192 on 8 waves: 4 x loads
+  // for each of waves 0-3, 3 W loads for each of waves 4-7).
+  constexpr bool EVEN = XL % NW == 0 && WL % NW == 0;
+  constexpr int NXW = NW / 2;
+  static_assert(EVEN || (XL % NXW == 0 && WL % (NW - NXW) == 0), "loads must split over the waves");
+  constexpr int XPW = EVEN ? XL / NW : XL / NXW;         // x loads per (x-loading) wave per stage
+  constexpr int WPW = EVEN ? WL / NW : WL / (NW - NXW);  // W loads per (W-loading) wave per stage
+  constexpr int LPW = EVEN ? XPW + WPW : (XPW > WPW ? XPW : WPW);  // offsets a wave keeps
   constexpr int WCH = BN / 8;                  // 16-B chunks per W row
   constexpr int SPS = 512 / 32;                // stages per segment (KC = 512)
   __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
@@ -594,19 +604,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, BM * BN <= 128 * 128 ? 2 : 1) void 
   const i32x4_t wr = make_rsrc_words(W, (uint32_t)((size_t)K * N * 2));
   const int nst = K / 32;
 
-  // this wave's loads: x regions wave * XPW + j (16 rows of 64 B each) and
-  // W regions wave * WPW + j (1 KB of the 32 x BN slab)
+  // this wave's loads: x regions xi + j (16 rows of 64 B each) and W
+  // regions wi + j (1 KB of the 32 x BN slab); not EVEN, a wave loads only x
+  // (xw) or only W
+  const bool xw = EVEN || wave < NXW;  // uniform per wave
+  const int xi = EVEN ? wave * XPW : wave * XPW;
+  const int wi = EVEN ? wave * WPW : (wave - NXW) * WPW;
+  auto x_off = [&](int region) {
+    const int c = region * 64 + lane, r = c >> 2, lc = (c & 3) ^ ((r >> 2) & 3);
+    return ((uint32_t)(m0 + r) * (uint32_t)K + (uint32_t)(lc * 8)) * 2u;
+  };
+  auto w_off = [&](int region) {
+    const int c = region * 64 + lane, r = c / WCH;
+    const int lc = (c % WCH) ^ wide_wsw<BN>(r);
+    return ((uint32_t)r * (uint32_t)N + (uint32_t)(n0 + lc * 8)) * 2u;
+  };
   uint32_t goff[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
-    if (j < XPW) {
-      const int c = (wave * XPW + j) * 64 + lane, r = c >> 2, lc = (c & 3) ^ ((r >> 2) & 3);
-      goff[j] = ((uint32_t)(m0 + r) * (uint32_t)K + (uint32_t)(lc * 8)) * 2u;
-    } else {
-      const int c = (wave * WPW + j - XPW) * 64 + lane, r = c / WCH;
-      const int lc = (c % WCH) ^ wide_wsw<BN>(r);
-      goff[j] = ((uint32_t)r * (uint32_t)N + (uint32_t)(n0 + lc * 8)) * 2u;
-    }
+    if constexpr (EVEN)
+      goff[j] = j < XPW ? x_off(xi + j) : w_off(wi + j - XPW);
+    else
+      goff[j] = xw ? x_off(xi + (j < XPW ? j : 0)) : w_off(wi + (j < WPW ? j : 0));
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(BI_LDS void*)lds;
   // loads of stage st into ring slot st % NS; the stage's advance along K
@@ -618,13 +637,33 @@ __global__ __launch_bounds__(64 * WGM * WGN, BM * BN <= 128 * 128 ? 2 : 1) void 
     const uint32_t base = lds0 + (uint32_t)((st % NS) * STAGE * 2);
     const uint32_t sx = valid ? (uint32_t)(st * 64) : 0x80000000u;
     const uint32_t sw = valid ? (uint32_t)st * 32u * (uint32_t)N * 2u : 0x80000000u;
+    if constexpr (EVEN) {
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      if (j < XPW)
-        lds_dma16_so(xr, goff[j], sx, base + (uint32_t)((wave * XPW + j) * 1024));
-      else
-        lds_dma16_so(wr, goff[j], sw, base + (uint32_t)(XS * 2 + (wave * WPW + j - XPW) * 1024));
+      for (int j = 0; j < LPW; ++j) {
+        if (j < XPW)
+          lds_dma16_so(xr, goff[j], sx, base + (uint32_t)((xi + j) * 1024));
+        else
+          lds_dma16_so(wr, goff[j], sw, base + (uint32_t)(XS * 2 + (wi + j - XPW) * 1024));
+      }
+    } else if (xw) {
+#pragma unroll
+      for (int j = 0; j < XPW; ++j)
+        lds_dma16_so(xr, goff[j], sx, base + (uint32_t)((xi + j) * 1024));
+    } else {
+#pragma unroll
+      for (int j = 0; j < WPW; ++j)
+        lds_dma16_so(wr, goff[j], sw, base + (uint32_t)(XS * 2 + (wi + j) * 1024));
     }
+  };
+  // s_waitcnt vmcnt(loads of n stages) + s_barrier for this wave's count
+  auto wait_stages = [&](auto n) {
+    constexpr int S = decltype(n)::value;
+    if constexpr (EVEN)
+      wait_vm_barrier<LPW * S>();
+    else if (xw)
+      wait_vm_barrier<XPW * S>();
+    else
+      wait_vm_barrier<WPW * S>();
   };
 
   // fragment addresses (bytes in LDS) in the ring slot of the stage being
@@ -699,7 +738,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, BM * BN <= 128 * 128 ? 2 : 1) void 
     // st + NS - 2 may be in flight); after the barrier every wave's have,
     // and every wave has consumed the fragments of stage st - 1, so that
     // slot takes stage st + NS - 1
-    wait_vm_barrier<LPW * (NS - 3)>();
+    wait_stages(std::integral_constant<int, NS - 3>{});
     dma(st + NS - 1);
     advance(st);
     __builtin_amdgcn_sched_barrier(0);
@@ -729,7 +768,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, BM * BN <= 128 * 128 ? 2 : 1) void 
   // prologue: stages 0 .. NS - 2 in flight; stage 0's fragments read
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0) dma(s0);
-  wait_vm_barrier<LPW * (NS - 2)>();
+  wait_stages(std::integral_constant<int, NS - 2>{});
 #pragma unroll
   for (int tt = 0; tt < SN; ++tt) read_w(tt);
 #pragma unroll
@@ -763,6 +802,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, BM * BN <= 128 * 128 ? 2 : 1) void 
 }
 
 template __global__ void gemm_wide_kernel<128, 128, 2, 2, 5, true>(const uint16_t*,
+                                                                   const uint16_t*, uint16_t*, int,
+                                                                   int, int, int, int, int, int);
+template __global__ void gemm_wide_kernel<256, 192, 4, 2, 5, true>(const uint16_t*,
                                                                    const uint16_t*, uint16_t*, int,
                                                                    int, int, int, int, int, int);
 template __global__ void gemm_wide_kernel<256, 256, 2, 4, 4, false>(const uint16_t*,
@@ -841,17 +883,28 @@ static int tile_remap(int64_t tm, int64_t tn) {
   return (tm % 8 == 0 && tn % 4 == 0) ? 3 : (tn % 8 == 0) ? 2 : ((tm * tn) % 8 == 0) ? 1 : 0;
 }
 
-// The invariant schedule on 256 x 128 tiles.  When they take more than one
-// round of the CUs and the last round is partial, the tile columns of that
-// round are computed as 128 x 128 tiles instead (twice as many, each half the
-// work, one per CU in a second launch): e.g. qkv at M = 2048, 384 tiles, runs
-// 256 of 256 x 128 and then 256 of 128 x 128 where it ran two rounds of
-// 256 x 128.  Both kernels compute every output with the same schedule, so
-// which one computes a column changes no bits.
+// The invariant schedule on 256 x 128 tiles.  Where those leave a partial
+// last round of the CUs but 256 x 192 tiles make whole rounds, the 256 x 192
+// register-fold tile runs instead (8 waves of 64 x 96).  Otherwise, when the
+// 256 x 128 tiles take more than one round and the last is partial, the tile
+// columns of that round are computed as 128 x 128 tiles (twice as many, each
+// half the work, one per CU in a second launch): e.g. gate_up at M = 1024,
+// 896 tiles, runs 768 of 256 x 128 and then 256 of 128 x 128.  All these
+// kernels compute every output with the same schedule, so which one computes
+// a column changes no bits.
 static int launch_tile_invariant(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M,
                                  int64_t N, int64_t K, int64_t tm, int64_t tn, hipStream_t stream) {
   const int64_t C = 256;  // rounds of a 256-CU chip (a constant: the plan reads no device state)
   const int64_t T = tm * tn;
+  // 256 x 192 tiles where they make whole rounds and 256 x 128 tiles do not
+  // (qkv at M = 2048: 256 tiles, one round, where 256 x 128 makes 384)
+  if (T % C != 0 && N % 192 == 0 && (tm * (N / 192)) % C == 0) {
+    const int64_t tn3 = N / 192;
+    hipLaunchKernelGGL((gemm_wide_kernel<256, 192, 4, 2, 5, true>), dim3((unsigned)(tm * tn3)),
+                       dim3(512), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)tm, (int)tn3,
+                       tile_remap(tm, tn3), 0);
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+  }
   int64_t k = 0;  // tile columns moved to the 128 x 128 launch
   if (T > C && T % C != 0) {
     k = ceil_div(T % C, tm);

@@ -206,15 +206,18 @@ def test_fold128_path_ragged_shapes(gpu, M, N, K):
     check_close_bf16(bits(y[rows]), oracle.gemm(bits(x[rows]), bits(w)), what=f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(2048, 6144, 4096), (1024, 28672, 4096), (1536, 6144, 4096),
-                                   (1100, 7104, 1056)])
+@pytest.mark.parametrize("M,N,K", [(2048, 6144, 4096), (2000, 6144, 4128), (1024, 28672, 4096),
+                                   (1536, 6144, 4096), (1100, 7104, 1056)])
 def test_partial_round_retiled(gpu, M, N, K):
-    """256 x 128 tiles that leave a partial last round on 256 CUs (384, 896,
-    288 and 280 tiles): the tile columns of that round run as 128 x 128
-    tiles in a second launch.  The last shape has a last tile row of 76 rows,
-    a last tile column of 64 columns and a one-K-block last segment.  Rows
-    match the skinny path and single-row calls bit for bit across the seam
-    between the two launches' columns, and the oracle within tolerance."""
+    """256 x 128 tiles that leave a partial last round on 256 CUs.  At
+    N = 6144 and 8 tile rows, 256 x 192 tiles make one whole round and run
+    instead (the second shape with a last tile row of 208 rows and a
+    one-K-block last segment).  Otherwise (896, 288 and 280 tiles) the tile
+    columns of the last round run as 128 x 128 tiles in a second launch; the
+    last shape has a last tile row of 76 rows, a last tile column of 64
+    columns and a one-K-block last segment.  Rows match the skinny path and
+    single-row calls bit for bit, across the seam between the two launches'
+    columns where there is one, and the oracle within tolerance."""
     x, w = synth.gemm_inputs(M, K, N, seed=M + 7 * K, device=DEV)
     assert gpu.gemm_workspace_bytes(M, N, K) == 0
     y = gpu.gemm(x, w)
