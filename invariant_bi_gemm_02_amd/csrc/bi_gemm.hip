@@ -10,15 +10,15 @@
 // in the fixed index order, with no float atomics anywhere; the K split is
 // the same whatever M is.  The arithmetic unit of the schedule is a 16-row
 // matrix-core sub-tile, padded with zero rows past M; how many sub-tiles
-// one workgroup takes (16, 32, 64 or 256 rows) and which kernel runs them
-// follow M, which moves work between workgroups and never changes a bit.
+// one workgroup takes (16, 32, 64, 128 or 256 rows) and which kernel runs
+// them follow M, which moves work between workgroups and never changes a bit.
 //
 // Several kernels implement that schedule; which ones run depends on (M, N),
 // and the bits never do (all issue the same matrix-core instruction on the
 // same operands in the same order, start every segment from +0, and fold the
 // segments with the same fp32 adds in index order):
 //   gemm_skinny_kernel  M <= 64 (weight streaming, HBM bound): one 512-lane
-//                       workgroup per (64-column tile, segment) writes the
+//                       workgroup per (128-column tile, segment) writes the
 //                       segment sum to the workspace.
 //   gemm_fold_kernel    adds workspace segment sums in index order, narrows.
 //   gemm_tile_kernel    M > 64 (matrix-core bound): 256x128 output tiles, all
@@ -26,6 +26,10 @@
 //                       fill the chip, one workgroup per (tile, run of
 //                       consecutive segments) writes each segment's sum for
 //                       gemm_fold_kernel instead.
+//   gemm_wide_kernel    other tile shapes on a ring of one K-block per stage:
+//                       128x128 and 256x192 with every segment folded in
+//                       registers (where 256x128 tiles would leave CUs idle
+//                       or a partial last round), 256x256 for the fast twin.
 // Padding rows (>= M) load as zero through the buffer range check and are
 // never stored.
 //
@@ -35,9 +39,10 @@
 // (ds_read_b64_tr_b16), which hands each lane one column.
 //
 // The fast twin reuses these kernels with a schedule picked from M and the
-// CU count: at M > 64 the tile kernel runs one accumulation chain over all of
-// K (no segments), sliced in K only as far as needed to fill the chip; at
-// M <= 64 it runs the invariant kernels unchanged.
+// CU count: at M > 64 one accumulation chain over all of K (no segments), on
+// 256x256 tiles where those fill the chip, else on 256x128 tiles sliced in K
+// only as far as needed to fill it; at M <= 64 it runs the invariant kernels
+// unchanged.
 #include <type_traits>
 
 #include "bi_common.h"
