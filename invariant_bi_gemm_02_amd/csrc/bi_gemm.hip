@@ -832,10 +832,20 @@ static constexpr int TILE_MIN_TILES = 192;  // fewer tiles than this leave CUs i
 // when there are enough of them; else 128 x 128 tiles with every segment in
 // registers when those fill the chip (o and down at M = 1024: 256 tiles
 // instead of 128, and no segment sums through memory); else the K-slice
-// path.  The fast twin has no 128 x 128 path (it slices K freely instead).
+// path.  The fast twin has no 128 x 128 path at M > 64 (it slices K freely
+// instead).  M <= 64: the skinny kernel, or 128 x 128 tiles for wide N.
 enum class GemmPath { Tile, Fold128, TileSlice, Skinny };
+static constexpr int FOLD128_MIN_M = 16;  // below it the skinny kernel streams W faster
 static GemmPath gemm_path(int64_t M, int64_t N, bool fast) {
-  if (M <= SKINNY_MAX_M) return GemmPath::Skinny;
+  if (M <= SKINNY_MAX_M) {
+    // 16-64 rows with enough 128 x 128 tiles to fill the chip (gate_up, an LM
+    // head): the register-fold tiles beat the skinny kernel and its fold
+    // launch (gate_up at M = 64: 55 against 71 us).  The fast twin follows
+    // the same choice at these M, as it does for the skinny kernel.
+    if (M >= FOLD128_MIN_M && ceil_div(M, 128) * ceil_div(N, 128) >= TILE_MIN_TILES)
+      return GemmPath::Fold128;
+    return GemmPath::Skinny;
+  }
   if (ceil_div(M, TILE_BM) * ceil_div(N, TL_BN) >= TILE_MIN_TILES) return GemmPath::Tile;
   if (!fast && ceil_div(M, 128) * ceil_div(N, 128) >= TILE_MIN_TILES) return GemmPath::Fold128;
   return GemmPath::TileSlice;

@@ -54,8 +54,8 @@ def test_noalloc_argument_checks(lib):
     assert lib.bi_gemm_noalloc(P(ok), P(ok), P(ok), 0, 64, 32, None) == -2
     assert lib.bi_gemm_noalloc(P(ok), P(ok), P(ok), 1, 64, 33, None) == -3
     assert lib.bi_gemm_noalloc(P(ok + 2), P(ok), P(ok), 1, 64, 32, None) == -3
-    assert lib.bi_gemm_workspace_bytes(64, 28672, 14336) > (64 << 20)
-    assert lib.bi_gemm_noalloc(P(ok), P(ok), P(ok), 64, 28672, 14336, None) == -6
+    assert lib.bi_gemm_workspace_bytes(64, 16384, 14336) > (64 << 20)
+    assert lib.bi_gemm_noalloc(P(ok), P(ok), P(ok), 64, 16384, 14336, None) == -6
 
 
 def P(v):
@@ -88,11 +88,15 @@ def test_gemm_argument_checks(lib):
     assert need == 8 * 32 * 4096 * 4
     assert lib.bi_gemm(P(ok), P(ok), P(ok), 32, 4096, 4096, P(ok), need - 16, None) == -4
     assert lib.bi_gemm(P(ok), P(ok), P(ok), 32, 4096, 4096, None, 0, None) == -4
-    # decode-sized M: segment sums always go through the workspace; large M
-    # folds in registers
+    # decode-sized M: segment sums go through the workspace, except at 16-64
+    # rows with enough 128 x 128 tiles to fill the chip; large M folds in
+    # registers
     assert lib.bi_gemm_workspace_bytes(1, 4096, 4096) == 8 * 1 * 4096 * 4
     assert lib.bi_gemm_workspace_bytes(16, 4096, 14336) == 28 * 16 * 4096 * 4
-    assert lib.bi_gemm_workspace_bytes(16, 28672, 4096) == 8 * 16 * 28672 * 4
+    assert lib.bi_gemm_workspace_bytes(15, 28672, 4096) == 8 * 15 * 28672 * 4
+    assert lib.bi_gemm_workspace_bytes(16, 28672, 4096) == 0
+    assert lib.bi_gemm_workspace_bytes(64, 16384, 4096) == 8 * 64 * 16384 * 4
+    assert lib.bi_gemm_workspace_bytes(64, 24576, 4096) == 0
     assert lib.bi_gemm_workspace_bytes(2048, 4096, 4096) == 0
 
 

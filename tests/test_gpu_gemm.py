@@ -248,6 +248,25 @@ def test_random_shapes_vs_oracle_and_single_rows(gpu, seed):
         assert same_bits(gpu.gemm(xd[r:r + 1].contiguous(), wd), y[r:r + 1]), f"row {r}"
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 28672, 4096), (17, 24640, 1056), (40, 25600, 4640),
+                                   (64, 28672, 14336), (48, 49216, 4096)])
+def test_decode_rows_on_fold128_tiles(gpu, M, N, K):
+    """16-64 rows with wide N (at least 192 tiles of 128 x 128: gate_up, an
+    vocabulary-wide LM head) run on the 128 x 128 register-fold tiles instead of the skinny
+    kernel; shapes with a half-empty last tile column (N % 128 == 64) and a
+    one-K-block last segment included.  Every row matches the same row
+    computed alone (the skinny path) bit for bit, and sampled rows the
+    oracle within tolerance."""
+    x, w = synth.gemm_inputs(M, K, N, seed=M * 7 + K, device=DEV)
+    assert gpu.gemm_workspace_bytes(M, N, K) == 0
+    y = gpu.gemm(x, w)
+    for r in range(M):
+        assert same_bits(gpu.gemm(x[r:r + 1].contiguous(), w), y[r:r + 1]), f"row {r}"
+    torch.cuda.synchronize()
+    rows = [0, M // 2, M - 1]
+    check_close_bf16(bits(y[rows]), oracle.gemm(bits(x[rows]), bits(w)), what=f"{M}x{N}x{K}")
+
+
 def test_run_to_run_and_row_permutation(gpu):
     x, w = synth.gemm_inputs(300, 4096, 4096, seed=4, device=DEV)
     base = gpu.gemm(x, w)

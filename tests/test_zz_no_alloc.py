@@ -29,10 +29,11 @@ def bits(t):
 
 
 @pytest.mark.parametrize("first,second", [
-    ((64, 28672, 4096), (5, 4096, 14336)),      # skinny path: 56 MiB, then 2.2 MiB
+    ((15, 28672, 14336), (5, 4096, 14336)),     # skinny path: 46 MiB, then 2.2 MiB
     ((200, 4096, 4096), (70, 1024, 1536)),      # K-slice tile path
     ((33, 6144, 4096), (1, 4096, 4096)),        # 32/64-row skinny, then one row
     ((2048, 4096, 4096), (300, 4096, 4096)),    # full tiles (no scratch), then K-slice
+    ((64, 28672, 4096), (17, 24576, 4096)),     # 128 x 128 tiles at decode M (no scratch)
 ])
 def test_noalloc_matches_bi_gemm_on_two_calls(gpu, first, second):
     lib = gpu.load()
@@ -53,7 +54,7 @@ def test_noalloc_matches_bi_gemm_on_two_calls(gpu, first, second):
 
 def test_noalloc_refuses_what_does_not_fit(gpu):
     lib = gpu.load()
-    M, N, K = 64, 28672, 14336                    # 28 segments x 64 x 28672 fp32 = 196 MiB
+    M, N, K = 64, 16384, 14336                    # 28 segments x 64 x 16384 fp32 = 112 MiB
     assert lib.bi_gemm_workspace_bytes(M, N, K) > (64 << 20)
     x = torch.zeros((M, K), dtype=torch.bfloat16, device=DEV)
     w = torch.zeros((K, N), dtype=torch.bfloat16, device=DEV)
