@@ -613,7 +613,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, BM * BN <= 128 * 128 ? 2 : 1) void 
   // regions wi + j (1 KB of the 32 x BN slab); not EVEN, a wave loads only x
   // (xw) or only W
   const bool xw = EVEN || wave < NXW;  // uniform per wave
-  const int xi = EVEN ? wave * XPW : wave * XPW;
+  const int xi = wave * XPW;
   const int wi = EVEN ? wave * WPW : (wave - NXW) * WPW;
   auto x_off = [&](int region) {
     const int c = region * 64 + lane, r = c >> 2, lc = (c & 3) ^ ((r >> 2) & 3);
