@@ -68,6 +68,45 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
     stg128(yr + base, scale8(ldg128(xr + base), ldg128(g + base), r));
 }
 
+// The same kernel for rows of at most 8 * 256 * CH values: the row's x and
+// the gain are loaded into registers once, before the reduction, and the
+// scaling reads them from there (one memory round trip, x read once).  The
+// lane sums, tree and scaling are those above, term for term.
+template <int CH>
+__global__ __launch_bounds__(256) void rmsnorm_reg_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ g,
+                                                          uint16_t* __restrict__ y, int H,
+                                                          float eps) {
+  __shared__ float wsum[4];
+  const int t = threadIdx.x;
+  const uint16_t* xr = x + (size_t)blockIdx.x * H;
+  uint16_t* yr = y + (size_t)blockIdx.x * H;
+  u32x4_t xv[CH], gv[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int base = 8 * (t + 256 * i);
+    if (base < H) {
+      xv[i] = ldg128(xr + base);
+      gv[i] = ldg128(g + base);
+    }
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+    if (8 * (t + 256 * i) < H) a = sumsq8(xv[i], a);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) a = a + __shfl_xor(a, o, 64);
+  if ((t & 63) == 0) wsum[t >> 6] = a;
+  __syncthreads();
+  const float ss = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  const float r = inv_rms(ss, H, eps);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int base = 8 * (t + 256 * i);
+    if (base < H) stg128(yr + base, scale8(xv[i], gv[i], r));
+  }
+}
+
 // Fast twin for large M: one wave per row, four rows per workgroup.
 __global__ __launch_bounds__(256) void rmsnorm_row_per_wave_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ g, uint16_t* __restrict__ y,
@@ -141,6 +180,15 @@ int launch_rmsnorm(const uint16_t* x, const uint16_t* g, uint16_t* y, int64_t M,
   if (fast && M >= 1024) {
     hipLaunchKernelGGL(rmsnorm_row_per_wave_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0,
                        stream, x, g, y, (int)M, (int)H, eps);
+  } else if (H <= 2048) {
+    hipLaunchKernelGGL(rmsnorm_reg_kernel<1>, dim3((unsigned)M), dim3(256), 0, stream, x, g, y,
+                       (int)H, eps);
+  } else if (H <= 4096) {
+    hipLaunchKernelGGL(rmsnorm_reg_kernel<2>, dim3((unsigned)M), dim3(256), 0, stream, x, g, y,
+                       (int)H, eps);
+  } else if (H <= 8192) {
+    hipLaunchKernelGGL(rmsnorm_reg_kernel<4>, dim3((unsigned)M), dim3(256), 0, stream, x, g, y,
+                       (int)H, eps);
   } else {
     hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, g, y, (int)H,
                        eps);
