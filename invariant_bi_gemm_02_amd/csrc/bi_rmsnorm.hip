@@ -107,7 +107,10 @@ __global__ __launch_bounds__(256) void rmsnorm_reg_kernel(const uint16_t* __rest
   }
 }
 
-// Fast twin for large M: one wave per row, four rows per workgroup.
+// Fast twin for large M: one wave per row, four rows per workgroup; rows of
+// up to 8 * 64 * CH values stay in registers between the two passes (CH = 0:
+// any H, read twice).
+template <int CH>
 __global__ __launch_bounds__(256) void rmsnorm_row_per_wave_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ g, uint16_t* __restrict__ y,
     int M, int H, float eps) {
@@ -117,12 +120,35 @@ __global__ __launch_bounds__(256) void rmsnorm_row_per_wave_kernel(
   const uint16_t* xr = x + (size_t)row * H;
   uint16_t* yr = y + (size_t)row * H;
   float a = 0.0f;
-  for (int base = 8 * lane; base < H; base += 8 * 64) a = sumsq8(ldg128(xr + base), a);
+  if constexpr (CH > 0) {
+    u32x4_t xv[CH], gv[CH];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) a = a + __shfl_xor(a, o, 64);
-  const float r = inv_rms(a, H, eps);
-  for (int base = 8 * lane; base < H; base += 8 * 64)
-    stg128(yr + base, scale8(ldg128(xr + base), ldg128(g + base), r));
+    for (int i = 0; i < CH; ++i) {
+      const int base = 8 * (lane + 64 * i);
+      if (base < H) {
+        xv[i] = ldg128(xr + base);
+        gv[i] = ldg128(g + base);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      if (8 * (lane + 64 * i) < H) a = sumsq8(xv[i], a);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) a = a + __shfl_xor(a, o, 64);
+    const float r = inv_rms(a, H, eps);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int base = 8 * (lane + 64 * i);
+      if (base < H) stg128(yr + base, scale8(xv[i], gv[i], r));
+    }
+  } else {
+    for (int base = 8 * lane; base < H; base += 8 * 64) a = sumsq8(ldg128(xr + base), a);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) a = a + __shfl_xor(a, o, 64);
+    const float r = inv_rms(a, H, eps);
+    for (int base = 8 * lane; base < H; base += 8 * 64)
+      stg128(yr + base, scale8(ldg128(xr + base), ldg128(g + base), r));
+  }
 }
 
 // Residual add and the RMSNorm that follows it, in one pass over the row:
@@ -178,8 +204,13 @@ int launch_add_rmsnorm(const uint16_t* a, const uint16_t* b, const uint16_t* g, 
 int launch_rmsnorm(const uint16_t* x, const uint16_t* g, uint16_t* y, int64_t M, int64_t H,
                    float eps, hipStream_t stream, bool fast) {
   if (fast && M >= 1024) {
-    hipLaunchKernelGGL(rmsnorm_row_per_wave_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0,
-                       stream, x, g, y, (int)M, (int)H, eps);
+    const dim3 grid((unsigned)((M + 3) / 4));
+    if (H <= 4096)
+      hipLaunchKernelGGL(rmsnorm_row_per_wave_kernel<8>, grid, dim3(256), 0, stream, x, g, y,
+                         (int)M, (int)H, eps);
+    else
+      hipLaunchKernelGGL(rmsnorm_row_per_wave_kernel<0>, grid, dim3(256), 0, stream, x, g, y,
+                         (int)M, (int)H, eps);
   } else if (H <= 2048) {
     hipLaunchKernelGGL(rmsnorm_reg_kernel<1>, dim3((unsigned)M), dim3(256), 0, stream, x, g, y,
                        (int)H, eps);
