@@ -55,11 +55,11 @@
  *     H, or by (D, page size, Hq, Hkv).  How that schedule's fixed pieces
  *     (16-row matrix-core sub-tiles, 512-row K segments, 256-token chunks)
  *     are grouped into workgroups and kernels reads the batch as well: M
- *     picks 16/32/64-row, 128-row or 256-row workgroup tiles (256-row tiles
- *     whose last round on 256 compute units would be partial hand that
- *     round's columns to 128-row tiles in a second launch) and, where few
- *     tiles would leave compute units idle, how many consecutive segments
- *     one workgroup runs.  That grouping moves work between workgroups and
+ *     picks the skinny kernel's 16/32/64-row tiles or 64-, 128- or
+ *     256-row register-fold tiles (256-row tiles whose last round on 256
+ *     compute units would be partial hand that round's columns to 128-row
+ *     tiles in a second launch) and, where few tiles would leave compute
+ *     units idle, how many consecutive segments one workgroup runs.  That grouping moves work between workgroups and
  *     never changes an output bit; the GPU tests check every M of a
  *     1..2048 sweep against the M = 2048 rows bit for bit.  This is the
  *     reading taken of the Article's fixed-tile rule (section 4): what

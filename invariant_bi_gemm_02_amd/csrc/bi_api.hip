@@ -102,8 +102,8 @@ const char* bi_version(void) {
              "libbi 0.1.0 git=%s hip=%d.%d target=gfx950 "
              "gemm: mfma_f32_16x16x32_bf16 KB=%d KC=%d fold=left skinny_maxM=64 "
              "tile=256x128 whole_rounds=256x192 last_partial_round=128x128 "
-             "fold128_below=192tiles "
-             "slice_below=192tiles128; "
+             "fold128_below=192tiles fold64_below=192tiles128 "
+             "slice_below=192tiles64; "
              "rmsnorm: lanes=%d vec=8 butterfly=32..1 waves=((0+1)+2)+3 sqrt/div=IEEE; "
              "attn: chunk=%d tile=%d qk=mfma16x16x32 combine=chunk-order exp=__expf",
              BI_GIT_SHA, HIP_VERSION_MAJOR, HIP_VERSION_MINOR, bi::SCHED_GEMM_KB, bi::SCHED_GEMM_KC,

@@ -27,9 +27,10 @@
 //                       consecutive segments) writes each segment's sum for
 //                       gemm_fold_kernel instead.
 //   gemm_wide_kernel    other tile shapes on a ring of one K-block per stage:
-//                       128x128 and 256x192 with every segment folded in
-//                       registers (where 256x128 tiles would leave CUs idle
-//                       or a partial last round), 256x256 for the fast twin.
+//                       64x128, 128x128 and 256x192 with every segment
+//                       folded in registers (where 256x128 tiles would leave
+//                       CUs idle or a partial last round), 256x256 for the
+//                       fast twin.
 // Padding rows (>= M) load as zero through the buffer range check and are
 // never stored.
 //
@@ -529,10 +530,12 @@ __global__ __launch_bounds__(512, 2) void gemm_tile_kernel(
 // The same arithmetic as gemm_tile_kernel (one v_mfma_f32_16x16x32_bf16 per
 // 32-deep K-block, issued as y^T = W^T x^T; with FOLD, segments of 512 from
 // +0 folded left to right in registers) on other tile shapes:
-//   128 x 128, FOLD (4 waves of 64 x 64, two workgroups per CU): the
+//   128 x 128, FOLD (8 waves of 64 x 32, two workgroups per CU): the
 //     invariant schedule where 256 x 128 tiles would leave CUs idle but
 //     128 x 128 tiles fill the chip (e.g. o and down at M = 1024), so every
 //     segment stays in registers instead of going through the workspace;
+//   64 x 128, FOLD (4 waves of 32 x 64): the same where only tiles of 64
+//     rows fill the chip (o and down at M = 512);
 //   256 x 192, FOLD (8 waves of 64 x 96, one workgroup per CU, 251
 //     registers): the invariant schedule where 256 x 128 tiles would leave a
 //     partial round and 256 x 192 tiles make whole ones (qkv at M = 2048);
@@ -806,7 +809,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, BM * BN <= 128 * 128 ? 2 : 1) void 
   }
 }
 
-template __global__ void gemm_wide_kernel<128, 128, 2, 2, 5, true>(const uint16_t*,
+template __global__ void gemm_wide_kernel<64, 128, 2, 2, 6, true>(const uint16_t*,
+                                                                  const uint16_t*, uint16_t*, int,
+                                                                  int, int, int, int, int, int);
+template __global__ void gemm_wide_kernel<128, 128, 2, 4, 5, true>(const uint16_t*,
                                                                    const uint16_t*, uint16_t*, int,
                                                                    int, int, int, int, int, int);
 template __global__ void gemm_wide_kernel<256, 192, 4, 2, 5, true>(const uint16_t*,
@@ -831,10 +837,13 @@ static constexpr int TILE_MIN_TILES = 192;  // fewer tiles than this leave CUs i
 // Invariant schedule, M > 64: 256 x 128 tiles with every segment in registers
 // when there are enough of them; else 128 x 128 tiles with every segment in
 // registers when those fill the chip (o and down at M = 1024: 256 tiles
-// instead of 128, and no segment sums through memory); else the K-slice
-// path.  The fast twin has no 128 x 128 path at M > 64 (it slices K freely
-// instead).  M <= 64: the skinny kernel, or 128 x 128 tiles for wide N.
-enum class GemmPath { Tile, Fold128, TileSlice, Skinny };
+// instead of 128, and no segment sums through memory); else 64 x 128 tiles
+// the same way when those fill it (o and down at M = 512: 256 tiles, where
+// the K-slice path wrote and re-read 28 segment sums per output of down);
+// else the K-slice path.  The fast twin has no 128 x 128 or 64 x 128 path at
+// M > 64 (it slices K freely instead).  M <= 64: the skinny kernel, or
+// 128 x 128 tiles for wide N.
+enum class GemmPath { Tile, Fold128, Fold64, TileSlice, Skinny };
 static constexpr int FOLD128_MIN_M = 16;  // below it the skinny kernel streams W faster
 static GemmPath gemm_path(int64_t M, int64_t N, bool fast) {
   if (M <= SKINNY_MAX_M) {
@@ -848,6 +857,7 @@ static GemmPath gemm_path(int64_t M, int64_t N, bool fast) {
   }
   if (ceil_div(M, TILE_BM) * ceil_div(N, TL_BN) >= TILE_MIN_TILES) return GemmPath::Tile;
   if (!fast && ceil_div(M, 128) * ceil_div(N, 128) >= TILE_MIN_TILES) return GemmPath::Fold128;
+  if (!fast && ceil_div(M, 64) * ceil_div(N, 128) >= TILE_MIN_TILES) return GemmPath::Fold64;
   return GemmPath::TileSlice;
 }
 
@@ -888,7 +898,7 @@ static int64_t slice_kc(int64_t M, int64_t N, int64_t K, bool fast, int num_cus)
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, bool fast, int num_cus) {
   const GemmPath p = gemm_path(M, N, fast);
-  if (p == GemmPath::Tile || p == GemmPath::Fold128) return 0;
+  if (p == GemmPath::Tile || p == GemmPath::Fold128 || p == GemmPath::Fold64) return 0;
   const int64_t kc = p == GemmPath::TileSlice ? slice_kc(M, N, K, fast, num_cus) : BI_KC;
   return (size_t)ceil_div(K, kc) * (size_t)M * (size_t)N * sizeof(float);
 }
@@ -932,8 +942,8 @@ static int launch_tile_invariant(const uint16_t* x, const uint16_t* W, uint16_t*
   if (hipGetLastError() != hipSuccess) return BI_ERR_HIP;
   if (k == 0) return BI_OK;
   const int64_t tm2 = ceil_div(M, 128), tn2 = ceil_div(N - tn1 * TL_BN, 128);
-  hipLaunchKernelGGL((gemm_wide_kernel<128, 128, 2, 2, 5, true>), dim3((unsigned)(tm2 * tn2)),
-                     dim3(256), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)tm2, (int)tn2,
+  hipLaunchKernelGGL((gemm_wide_kernel<128, 128, 2, 4, 5, true>), dim3((unsigned)(tm2 * tn2)),
+                     dim3(512), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)tm2, (int)tn2,
                      tile_remap(tm2, tn2), (int)(tn1 * TL_BN));
   return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
 }
@@ -961,7 +971,14 @@ int launch_gemm(const uint16_t* x, const uint16_t* W, uint16_t* y, int64_t M, in
   const GemmPath p = gemm_path(M, N, fast);
   if (p == GemmPath::Fold128) {
     const int64_t tm = ceil_div(M, 128), tn = ceil_div(N, 128);
-    hipLaunchKernelGGL((gemm_wide_kernel<128, 128, 2, 2, 5, true>), dim3((unsigned)(tm * tn)),
+    hipLaunchKernelGGL((gemm_wide_kernel<128, 128, 2, 4, 5, true>), dim3((unsigned)(tm * tn)),
+                       dim3(512), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)tm, (int)tn,
+                       tile_remap(tm, tn), 0);
+    return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;
+  }
+  if (p == GemmPath::Fold64) {
+    const int64_t tm = ceil_div(M, 64), tn = ceil_div(N, 128);
+    hipLaunchKernelGGL((gemm_wide_kernel<64, 128, 2, 2, 6, true>), dim3((unsigned)(tm * tn)),
                        dim3(256), 0, stream, x, W, y, (int)M, (int)N, (int)K, (int)tm, (int)tn,
                        tile_remap(tm, tn), 0);
     return hipGetLastError() == hipSuccess ? BI_OK : BI_ERR_HIP;

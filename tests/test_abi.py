@@ -89,14 +89,18 @@ def test_gemm_argument_checks(lib):
     assert lib.bi_gemm(P(ok), P(ok), P(ok), 32, 4096, 4096, P(ok), need - 16, None) == -4
     assert lib.bi_gemm(P(ok), P(ok), P(ok), 32, 4096, 4096, None, 0, None) == -4
     # decode-sized M: segment sums go through the workspace, except at 16-64
-    # rows with enough 128 x 128 tiles to fill the chip; large M folds in
-    # registers
+    # rows with enough 128 x 128 tiles to fill the chip; mid M with too few
+    # tiles of 128 and of 64 rows slices K through the workspace; larger M
+    # folds in registers
     assert lib.bi_gemm_workspace_bytes(1, 4096, 4096) == 8 * 1 * 4096 * 4
     assert lib.bi_gemm_workspace_bytes(16, 4096, 14336) == 28 * 16 * 4096 * 4
     assert lib.bi_gemm_workspace_bytes(15, 28672, 4096) == 8 * 15 * 28672 * 4
     assert lib.bi_gemm_workspace_bytes(16, 28672, 4096) == 0
     assert lib.bi_gemm_workspace_bytes(64, 16384, 4096) == 8 * 64 * 16384 * 4
     assert lib.bi_gemm_workspace_bytes(64, 24576, 4096) == 0
+    assert lib.bi_gemm_workspace_bytes(256, 4096, 14336) == 28 * 256 * 4096 * 4
+    assert lib.bi_gemm_workspace_bytes(512, 4096, 14336) == 0      # 256 tiles of 64 x 128
+    assert lib.bi_gemm_workspace_bytes(1024, 4096, 14336) == 0     # 256 tiles of 128 x 128
     assert lib.bi_gemm_workspace_bytes(2048, 4096, 4096) == 0
 
 

@@ -206,6 +206,27 @@ def test_fold128_path_ragged_shapes(gpu, M, N, K):
     check_close_bf16(bits(y[rows]), oracle.gemm(bits(x[rows]), bits(w)), what=f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(512, 4096, 14336), (330, 4160, 4640), (257, 6144, 1056),
+                                   (640, 4032, 4096)])
+def test_fold64_path_ragged_shapes(gpu, M, N, K):
+    """The 64 x 128 register-fold path (tiles of 256 and of 128 rows too few
+    to fill the chip, tiles of 64 rows enough): down at M = 512, then a last
+    tile row of 10, 1 and 64 rows, a last tile column of 64 columns
+    (N % 128 == 64) and a one-K-block last segment (K % 512 == 32).  Every
+    row of the first 64 matches the skinny path bit for bit (one call at
+    M = 64), sampled rows match single-row calls, and the oracle within
+    tolerance."""
+    x, w = synth.gemm_inputs(M, K, N, seed=M * 5 + K, device=DEV)
+    assert gpu.gemm_workspace_bytes(M, N, K) == 0      # every segment stays in registers
+    y = gpu.gemm(x, w)
+    assert same_bits(gpu.gemm(x[:64].contiguous(), w), y[:64])
+    rows = [0, 63, 64, M // 2, M - 1]
+    for r in rows:
+        assert same_bits(gpu.gemm(x[r:r + 1].contiguous(), w), y[r:r + 1]), f"row {r}"
+    torch.cuda.synchronize()
+    check_close_bf16(bits(y[rows]), oracle.gemm(bits(x[rows]), bits(w)), what=f"{M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(2048, 6144, 4096), (2000, 6144, 4128), (1024, 28672, 4096),
                                    (1536, 6144, 4096), (1100, 7104, 1056)])
 def test_partial_round_retiled(gpu, M, N, K):
