@@ -50,13 +50,13 @@ def on_stream(stream, fn, *args):
     return out
 
 
-@pytest.mark.parametrize("M,N", [(1, 4096), (16, 4096), (40, 4096), (300, 4096), (1024, 4096),
-                                 (2048, 4096), (2048, 6144), (1024, 28672)])
+@pytest.mark.parametrize("M,N", [(1, 4096), (16, 4096), (40, 4096), (300, 4096), (512, 4096),
+                                 (1024, 4096), (2048, 4096), (2048, 6144), (1024, 28672)])
 def test_gemm_bits_under_cu_masks(gpu, masked_streams, M, N):
-    """Every bi_gemm path: skinny (M = 1, 16, 40), K-slice (300), 128 x 128
-    register fold (1024 x 4096), 256 x 128 tiles (2048 x 4096), 256 x 192
-    tiles (2048 x 6144) and 256 x 128 tiles with the last partial round as
-    128 x 128 tiles (1024 x 28672)."""
+    """Every bi_gemm path: skinny (M = 1, 16, 40), K-slice (300), 64 x 128
+    register fold (512 x 4096), 128 x 128 register fold (1024 x 4096),
+    256 x 128 tiles (2048 x 4096), 256 x 192 tiles (2048 x 6144) and 256 x 128
+    tiles with the last partial round as 128 x 128 tiles (1024 x 28672)."""
     x, w = synth.gemm_inputs(M, 4096, N, seed=31 + M + N, device=DEV)
     ref = gpu.gemm(x, w)
     torch.cuda.synchronize()
@@ -112,13 +112,13 @@ def test_bits_under_concurrent_memory_load(gpu):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 6144), (2048, 4096, 6144), (256, 14336, 4096),
-                                   (1024, 14336, 4096)])
+                                   (512, 14336, 4096), (1024, 14336, 4096)])
 def test_gemm_hundred_repeats(gpu, M, K, N):
     """Bitwise stable over 100 calls: the skinny path, the 256 x 192 tile
     path (qkv at M = 2048), the K-slice path with runs of four segments per
     workgroup (down at M = 256), whose segment-sum stores go out while the
-    load ring keeps running, and the 128 x 128 register-fold path (down at
-    M = 1024)."""
+    load ring keeps running, and the 64 x 128 and 128 x 128 register-fold
+    paths (down at M = 512 and 1024)."""
     x, w = synth.gemm_inputs(M, K, N, seed=36, device=DEV)
     ref = gpu.gemm(x, w)
     outs = [gpu.gemm(x, w) for _ in range(100)]

@@ -34,6 +34,7 @@ def bits(t):
     ((33, 6144, 4096), (1, 4096, 4096)),        # 32/64-row skinny, then one row
     ((2048, 4096, 4096), (300, 4096, 4096)),    # full tiles (no scratch), then K-slice
     ((64, 28672, 4096), (17, 24576, 4096)),     # 128 x 128 tiles at decode M (no scratch)
+    ((512, 4096, 14336), (128, 4096, 14336)),   # 64 x 128 tiles (no scratch), then K-slice (56 MiB)
 ])
 def test_noalloc_matches_bi_gemm_on_two_calls(gpu, first, second):
     lib = gpu.load()
