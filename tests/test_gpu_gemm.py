@@ -146,6 +146,25 @@ def test_m_sweep_bitwise_and_sampled_oracle(gpu, name, K, N):
     check_close_bf16(got, want, what=f"{name} sampled rows")
 
 
+@pytest.mark.parametrize("name,K,N", synth.LLAMA3_8B_LINEARS)
+def test_every_m_from_1_to_2048_bitwise(gpu, name, K, N):
+    """Every M from 1 to 2048, not only the sweep's: the leading M rows of
+    the M = 2048 run, bit for bit.  This crosses every boundary of the plan
+    on each linear (skinny kernel at 16/32/64 rows, 128 x 128 tiles for wide N
+    at 16-64 rows, K-slice, 64 x 128 and 128 x 128 register-fold tiles,
+    256 x 128 tiles with and without a re-tiled last round, 256 x 192 whole
+    rounds).  Mismatch flags stay on the device until the end."""
+    x, w = synth.gemm_inputs(2048, K, N, seed=13, device=DEV)
+    ref = gpu.gemm(x, w)
+    ref16 = ref.view(torch.int16)
+    flags = []
+    for M in range(1, 2049):
+        y = gpu.gemm(x[:M].contiguous(), w)
+        flags.append((y.view(torch.int16) != ref16[:M]).any())
+    bad = torch.stack(flags).nonzero().flatten().add(1).tolist()
+    assert not bad, f"{name}: M = {bad[:10]} differ from the M = 2048 rows"
+
+
 @pytest.mark.parametrize("M,N,K", [(2048, 3136, 544), (1500, 4224, 1056), (700, 8256, 96),
                                    (2048, 3136, 640), (2048, 3136, 576), (1500, 4224, 1216)])
 def test_tile_path_ragged_shapes(gpu, M, N, K):
