@@ -331,13 +331,19 @@ def run_extras(torch, bi, synth, dev, args, M, acts, wsets):
         ax = make_acts(torch, synth, Mx, dev, seed=1) if Mx != M else acts
         ox = {name: torch.empty((Mx, N), dtype=torch.bfloat16, device=dev)
               for name, K, N in LINEARS}
-        row = {"bi": {}, "fast": {}}
+        row = {"bi": {}, "fast": {}, "vendor": {}}
         for name, K, N in LINEARS:
             cp = wcopies[name]
             reps = len(cp) if Mx >= 1024 else max(20, 2 * len(cp))
             calls = [(ax[name], cp[i % len(cp)], ox[name]) for i in range(reps)]
             row["bi"][name], row["fast"][name] = paired_graph_time_us(
                 torch, bi.gemm, bi.gemm_fast, calls)
+            # the vendor library's bf16 matmul (hipBLASLt through torch, not
+            # batch-invariant) on the same calls: a reference that is not one
+            # of this library's kernels, also where the fast twin is the
+            # invariant kernel itself
+            row["vendor"][name] = graph_time_us(
+                torch, lambda a, b, out: torch.matmul(a, b, out=out), calls)
         # at M <= 64 the fast twin runs the invariant kernels (streaming W is
         # the bound and the invariant schedule already streams it at full
         # width), so no overhead is claimed there
@@ -345,8 +351,10 @@ def run_extras(torch, bi, synth, dev, args, M, acts, wsets):
         lin = {}
         for name, K, N in LINEARS:
             tb, tf = row["bi"][name], row["fast"][name]
+            tv = row["vendor"][name]
             lin[name] = {"us": tb, "fast_us": tf, "same_kernel": same,
                          "overhead_pct": None if same else (tb / tf - 1) * 100,
+                         "vendor_us": tv, "vs_vendor_pct": (tb / tv - 1) * 100,
                          "tflops": gemm_flops(Mx, K, N) / (tb * 1e-6) / 1e12,
                          "gbs": gemm_bytes(Mx, K, N) / (tb * 1e-6) / 1e9,
                          "weight_copies": len(wcopies[name])}
@@ -357,11 +365,13 @@ def run_extras(torch, bi, synth, dev, args, M, acts, wsets):
                 lin[name]["frac_of_read_ceiling"] = read_us[name] / tb
         tot_b = sum(row["bi"].values())
         tot_f = sum(row["fast"].values())
+        tot_v = sum(row["vendor"].values())
         byt = sum(gemm_bytes(Mx, K, N) for _, K, N in LINEARS)
         fl = sum(gemm_flops(Mx, K, N) for _, K, N in LINEARS)
         per[str(Mx)] = {"linears": lin, "step_us": tot_b, "fast_step_us": tot_f,
                         "same_kernel": same,
                         "overhead_pct": None if same else (tot_b / tot_f - 1) * 100,
+                        "vendor_step_us": tot_v, "vs_vendor_pct": (tot_b / tot_v - 1) * 100,
                         "gbs": byt / (tot_b * 1e-6) / 1e9,
                         "hbm_frac": byt / (tot_b * 1e-6) / 1e9 / HBM_PEAK_GBS,
                         "tflops": fl / (tot_b * 1e-6) / 1e12,
@@ -490,6 +500,10 @@ def main():
                     "back-to-back calls of each, replayed alternately (medians of five rounds)",
             "by_M": {k: v["overhead_pct"] for k, v in extras["by_M"].items()},
             "same_kernel_M": [int(k) for k, v in extras["by_M"].items() if v["same_kernel"]],
+            "vs_vendor_by_M": {k: v["vs_vendor_pct"] for k, v in extras["by_M"].items()},
+            "vendor": "t_bi / t_vendor - 1 of the same step, the vendor being torch's bf16 "
+                      "matmul (hipBLASLt, not batch-invariant) replayed from a graph of the "
+                      "same calls",
             "pages": PAGES_OVERHEAD,
         }
         extras["fast_step_sequential"] = {
