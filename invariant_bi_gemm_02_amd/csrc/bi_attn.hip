@@ -99,8 +99,8 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(
         if (page >= 0 && page < num_pages) {
           const size_t kofs = (((size_t)page * 2 + 0) * Hkv + hk) * (APS * AD) + (t % APS) * AD + dc * 8;
           const size_t vofs = kofs + (size_t)Hkv * APS * AD;
-          kr[i] = ldg128(kv + kofs);
-          vr[i] = ldg128(kv + vofs);
+          kr[i] = ldg128_nt(kv + kofs);  // each K/V tile is read once per kv head
+          vr[i] = ldg128_nt(kv + vofs);
         }
       }
     }

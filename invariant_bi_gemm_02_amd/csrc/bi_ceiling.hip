@@ -65,8 +65,9 @@ int launch_mfma_ceiling(float* out, int64_t iters, int64_t workgroups, hipStream
 
 // Streaming read: every 16-byte chunk of p[0 .. n16) is loaded once, four
 // chunks per lane per round (consecutive lanes on consecutive chunks, 1 KB per
-// wave instruction), and XOR-ed into a register; each wave writes one word,
-// out[4 * blockIdx.x + wave], so that no load is optimised away.
+// wave instruction, non-temporal hint), and XOR-ed into a register; each wave
+// writes one word, out[4 * blockIdx.x + wave], so that no load is optimised
+// away.
 static constexpr int READ_UNROLL = 4;
 __global__ __launch_bounds__(256) void read_ceiling_kernel(const u32x4_t* __restrict__ p,
                                                            int64_t n16, uint32_t* __restrict__ out) {
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void read_ceiling_kernel(const u32x4_t* __rest
 #pragma unroll
     for (int u = 0; u < READ_UNROLL; ++u) {
       const int64_t i = base + (int64_t)u * 256;
-      v[u] = i < n16 ? p[i] : u32x4_t{0u, 0u, 0u, 0u};
+      v[u] = i < n16 ? ldg128_nt(p + i) : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < READ_UNROLL; ++u) acc ^= (v[u][0] ^ v[u][1]) ^ (v[u][2] ^ v[u][3]);

