@@ -59,9 +59,10 @@
  *     256-row register-fold tiles (256-row tiles whose last round on 256
  *     compute units would be partial hand that round's columns to 128-row
  *     tiles in a second launch) and, where few tiles would leave compute
- *     units idle, how many consecutive segments one workgroup runs.  That grouping moves work between workgroups and
- *     never changes an output bit; the GPU tests check every M of a
- *     1..2048 sweep against the M = 2048 rows bit for bit.  This is the
+ *     units idle, how many consecutive segments one workgroup runs.  That
+ *     grouping moves work between workgroups and never changes an output
+ *     bit; the GPU tests check every M from 1 to 2048 against the
+ *     M = 2048 rows bit for bit.  This is the
  *     reading taken of the Article's fixed-tile rule (section 4): what
  *     must not follow M is the arithmetic each output sees, not the
  *     launch shape.
